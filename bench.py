@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention, forward + backward, on one MI355X.
+
+One step = the whole hot path over one batch: fa_fwd, fa_bwd_preprocess,
+fa_bwd_dkdv, fa_bwd_dq (C ABI of libfa.so) on inputs already resident in HBM.
+Default workload: batch*heads = 32, N = 8192, d = 128, bf16, causal.
+
+Counted FLOPs per head (the metric's convention): forward 4 N^2 d, backward
+10 N^2 d, both halved when causal.  Prints one JSON line (rank 0).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
+MFMA_FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+METRIC = "fwd+bwd attention TFLOPS (bf16, causal, N=8192, d=128) + % of MFMA peak"
+
+
+def counted_flops(bh, n, d, causal):
+    half = 0.5 if causal else 1.0
+    fwd = 4.0 * n * n * d * bh * half
+    bwd = 10.0 * n * n * d * bh * half
+    return fwd, bwd
+
+
+def kernel_flops(bh, n, d, causal):
+    """Algorithmic MFMA flops per launch of each kernel (the contractions it
+    must perform, halved when causal): fwd S and PV (4 N^2 d); dK/dV kernel
+    S, dP, dV, dK (8 N^2 d); dQ kernel S, dP, dQ (6 N^2 d)."""
+    half = 0.5 if causal else 1.0
+    u = 2.0 * n * n * d * bh * half
+    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u}
+
+
+def kernel_bytes(bh, n, d, elt):
+    """Algorithmic HBM bytes per launch (each input read once, each output
+    written once)."""
+    t = bh * n * d * elt
+    r = bh * n * 4
+    return {"fwd": 4 * t + r, "preprocess": 2 * t + r, "dkdv": 6 * t + 2 * r, "dq": 5 * t + 2 * r}
+
+
+def cpu_baseline(bh, n, d, causal, budget_s=25.0):
+    """The fp64 oracle timed on host cores on a bounded sample of the same
+    workload: whole heads (forward + backward) until about `budget_s`."""
+    import numpy as np
+
+    import oracle
+    from workloads import cast_io, make_inputs, to_f64
+
+    cores = len(os.sched_getaffinity(0))
+    rng_inputs = make_inputs(1, n, d, seed=0)
+    q, k, v, do = (to_f64(t)[0] for t in cast_io(rng_inputs, "bf16"))
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.attention_forward(q, k, v, causal=causal)
+        oracle.attention_backward(q, k, v, do, causal=causal)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / heads * (heads + 1) > budget_s * 1.5:
+            break
+    fwd, bwd = counted_flops(heads, n, d, causal)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    return {
+        "value": (fwd + bwd) / el / 1e12,
+        "unit": "TFLOPS",
+        "cores": threads or cores,
+        "kind": "oracle",
+        "sample": f"{heads} of {bh} heads (N={n}, d={d}, {'causal' if causal else 'non-causal'}), "
+                  f"fp64 fwd+bwd, {el:.1f} s; host cores available: {cores}",
+        "seconds": el,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline_8192_d128")
+    ap.add_argument("--non-causal", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--fwd-tiles", default="0,0")
+    ap.add_argument("--dkdv-tiles", default="0,0")
+    ap.add_argument("--dq-tiles", default="0,0")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the path has no multi-GPU mode (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); heads would shard across GPUs with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_26_amd as fa
+    from workloads import WORKLOADS, cast_io, make_inputs
+
+    w = WORKLOADS[args.workload]
+    causal = not args.non_causal
+    bh, n, d = w.bh, w.n, w.d
+    elt = 2 if w.dtype == "bf16" else 4
+    ft = tuple(int(x) for x in args.fwd_tiles.split(","))
+    kt = tuple(int(x) for x in args.dkdv_tiles.split(","))
+    qt = tuple(int(x) for x in args.dq_tiles.split(","))
+    print(f"# workload {w.name}: bh={bh} n={n} d={d} {w.dtype} causal={causal}", file=sys.stderr, flush=True)
+
+    q, k, v, do = cast_io(make_inputs(bh, n, d, seed=0), w.dtype, "cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((bh, n), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    names = ("fwd", "preprocess", "dkdv", "dq")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, causal, None, *ft, stream=sptr)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_bwd_preprocess(o, do, delta, stream=sptr)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr)
+        if ev is not None:
+            ev[3].record(stream)
+        fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel = {nm: [] for nm in names}
+    step_ms = []
+    for ev in events:
+        for j, nm in enumerate(names):
+            per_kernel[nm].append(ev[j].elapsed_time(ev[j + 1]))
+        step_ms.append(ev[0].elapsed_time(ev[4]))
+    avg = {nm: sum(x) / len(x) for nm, x in per_kernel.items()}
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = sum(step_ms) / len(step_ms)
+
+    fwd_fl, bwd_fl = counted_flops(bh, n, d, causal)
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    tflops = (fwd_fl + bwd_fl) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = fwd_fl / (avg["fwd"] * 1e-3) / 1e12
+    bwd_ms = avg["preprocess"] + avg["dkdv"] + avg["dq"]
+    bwd_tf = bwd_fl / (bwd_ms * 1e-3) / 1e12
+
+    kfl = kernel_flops(bh, n, d, causal)
+    kby = kernel_bytes(bh, n, d, elt)
+    dom = max(("fwd", "dkdv", "dq"), key=lambda nm: avg[nm])
+    achieved = kfl[dom] / (avg[dom] * 1e-3) / 1e12
+    roofline = {
+        "kernel": dom,
+        "bound": "mfma",
+        "achieved": round(achieved, 1),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "avg_launch_ms": round(avg[dom], 4),
+        "algorithmic_flops_per_launch": kfl[dom],
+    }
+    kernels = {}
+    for nm in names:
+        ent = {"avg_ms": round(avg[nm], 4)}
+        if nm in kfl:
+            ent["tflops"] = round(kfl[nm] / (avg[nm] * 1e-3) / 1e12, 1)
+            ent["frac_mfma_peak"] = round(kfl[nm] / (avg[nm] * 1e-3) / 1e12 / peak, 4)
+        ent["hbm_gbs"] = round(kby[nm] / (avg[nm] * 1e-3) / 1e9, 1)
+        kernels[nm] = ent
+
+    base = None
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        base = cpu_baseline(bh, n, d, causal, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) Q, K, V, dO (numpy default_rng(0), cast to bf16)",
+        "config": {"workload": w.name, "batch_heads": bh, "seq_len": n, "head_dim": d,
+                   "causal": causal, "tiles": {"fwd": list(ft), "dkdv": list(kt), "dq": list(qt)}},
+        "pct_of_mfma_peak": round(100 * tflops / peak, 2),
+        "fwd_tflops": round(fwd_tf, 1),
+        "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
+        "bwd_tflops": round(bwd_tf, 1),
+        "bwd_pct_of_peak": round(100 * bwd_tf / peak, 2),
+        "event_ms_per_step": round(ev_ms, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,444 @@
+// float32 kernels with run-time tile sizes: forward, dK/dV and dQ.
+//
+// Same method as the bf16 kernels ("Assignment2: FlashAttention & Distributed
+// Data Parallel notes" (CS336) sections 1.2-1.4), computed entirely in fp32
+// with v_mfma_f32_16x16x4_f32 (no reduced-precision operands).  These serve
+// float32 I/O and any tiling the pages use: query tiles of 16-128 rows and
+// key tiles of 4-128 columns (multiples of 4, e.g. the 16 x 12 tiling of the
+// gradient check in "CS349E lecture 11, 03_flash_backward.py").  Every wave
+// owns 16 query rows (forward, dQ) or 16 key rows (dK/dV); a key tile that
+// is not a multiple of 16 occupies a 16-wide fragment whose extra columns are
+// masked, the same mechanism as the ragged end of the sequence.
+//
+// Tiles sit in LDS as [rows][D + 1] floats (odd row stride: the 16 rows a
+// fragment reads fall in distinct banks).
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+constexpr int kMaxBlk = 8;   // 128 / 16
+
+template <int D>
+__device__ __forceinline__ void stage_f32_rows(float* dst, const float* src, int rows_alloc,
+                                               int valid, int tid, int nthr) {
+  constexpr int LD = D + 1;
+  for (int e = tid; e < rows_alloc * D; e += nthr) {
+    const int r = e / D, c = e % D;
+    dst[r * LD + c] = (r < valid) ? src[(size_t)r * D + c] : 0.f;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512)
+void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                    const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
+                    int bh, int n, float scale_log2, int BR, int BC) {
+  extern __shared__ float smem[];
+  constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
+  const int BCP = (BC + 15) & ~15, nkb = BCP / 16;
+  float* ks = smem;
+  float* vs = smem + BCP * LD;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int ntq = (n + BR - 1) / BR;
+  const int head = blockIdx.x % bh;
+  const int q0 = (ntq - 1 - blockIdx.x / bh) * BR;
+  const int q0w = q0 + 16 * wave;
+  const int qr = q0w + l16;
+  const size_t hoff = (size_t)head * n * D;
+
+  // B operand of S^T = K Q^T: lane holds Q[qr][4st + g]
+  float qf[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) qf[st] = (qr < n) ? Q[hoff + (size_t)qr * D + 4 * st + g] : 0.f;
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, lsum = 0.f;
+
+  const int kend = CAUSAL ? min(n, q0 + BR) : n;
+  const int ntk = (kend + BC - 1) / BC;
+  for (int j = 0; j < ntk; ++j) {
+    const int j0 = j * BC;
+    const int valid = min(BC, n - j0);
+    __syncthreads();
+    stage_f32_rows<D>(ks, K + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
+    stage_f32_rows<D>(vs, V + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
+    __syncthreads();
+    if (CAUSAL && j0 > q0w + 15) continue;
+    // S^T: lane holds key j0 + 16kb + 4g + i, query qr
+    f32x4 s[kMaxBlk];
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < kMaxBlk; ++kb) {
+      if (kb < nkb) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < NST; ++st) c = mfma_f32(ks[(16 * kb + l16) * LD + 4 * st + g], qf[st], c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kl = 16 * kb + 4 * g + i;
+          if (kl >= valid || (CAUSAL && j0 + kl > qr)) c[i] = kNegInf;
+          mx = fmaxf(mx, c[i]);
+        }
+        s[kb] = c;
+      }
+    }
+    mx = wave_max_xor16_32(mx);
+    const float m_new = fmaxf(m, mx * scale_log2);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float corr = exp2_fast(m - m_use);
+    m = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kMaxBlk; ++kb) {
+      if (kb < nkb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2_fast(__builtin_fmaf(s[kb][i], scale_log2, -m_use));
+          s[kb][i] = p;
+          ps += p;
+        }
+      }
+    }
+    lsum = lsum * corr + ps;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= corr;
+    // O^T += V^T P^T: step t carries key 16kb + 4g + t for lane group g
+#pragma unroll
+    for (int kb = 0; kb < kMaxBlk; ++kb) {
+      if (kb < nkb) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float* vrow = vs + (16 * kb + 4 * g + t) * LD;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma_f32(vrow[16 * db + l16], s[kb][t], acc[db]);
+        }
+      }
+    }
+  }
+  const float lt = wave_sum_xor16_32(lsum);
+  if (qr < n) {
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      f32x4 o4 = acc[db] * inv;
+      *reinterpret_cast<f32x4*>(O + hoff + (size_t)qr * D + 16 * db + 4 * g) = o4;
+    }
+    if (g == 0) LSE[(size_t)head * n + qr] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512)
+void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                     const float* __restrict__ V, const float* __restrict__ dO,
+                     const float* __restrict__ LSE, const float* __restrict__ DELTA,
+                     float* __restrict__ dK, float* __restrict__ dV,
+                     int bh, int n, float scale, float scale_log2, int BR, int BC) {
+  extern __shared__ float smem[];
+  constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
+  float* qs = smem;
+  float* os = qs + BR * LD;
+  float* l2s = os + BR * LD;
+  float* dsm = l2s + BR;
+  const int nqb = BR / 16;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int head = blockIdx.x % bh;
+  const int k0 = (blockIdx.x / bh) * BC;
+  const int k0w = k0 + 16 * wave;
+  const int key = k0w + l16;
+  const bool key_ok = key < n && key < k0 + BC;
+  const size_t hoff = (size_t)head * n * D;
+
+  // B operands of S = Q K^T and dP = dO V^T: lane holds K[key][4st + g], V[key][4st + g]
+  float kf[NST], vf[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    kf[st] = key_ok ? K[hoff + (size_t)key * D + 4 * st + g] : 0.f;
+    vf[st] = key_ok ? V[hoff + (size_t)key * D + 4 * st + g] : 0.f;
+  }
+  f32x4 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int ntq = (n + BR - 1) / BR;
+  const int it0 = CAUSAL ? k0 / BR : 0;
+  for (int it = it0; it < ntq; ++it) {
+    const int i0 = it * BR;
+    const int valid = min(BR, n - i0);
+    __syncthreads();
+    stage_f32_rows<D>(qs, Q + hoff + (size_t)i0 * D, BR, valid, tid, nthr);
+    stage_f32_rows<D>(os, dO + hoff + (size_t)i0 * D, BR, valid, tid, nthr);
+    for (int r = tid; r < BR; r += nthr) {
+      l2s[r] = (r < valid) ? LSE[(size_t)head * n + i0 + r] * kLog2e : __builtin_inff();
+      dsm[r] = (r < valid) ? DELTA[(size_t)head * n + i0 + r] : 0.f;
+    }
+    __syncthreads();
+    if (CAUSAL && i0 + BR - 1 < k0w) continue;
+#pragma unroll
+    for (int qb = 0; qb < kMaxBlk; ++qb) {
+      if (qb < nqb) {
+        // S and dP: lane holds query i0 + 16qb + 4g + i, key `key`
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+        const float* qrow = qs + (16 * qb + l16) * LD;
+        const float* orow = os + (16 * qb + l16) * LD;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          s = mfma_f32(qrow[4 * st + g], kf[st], s);
+          dp = mfma_f32(orow[4 * st + g], vf[st], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = 16 * qb + 4 * g + i;
+          float p = exp2_fast(__builtin_fmaf(s[i], scale_log2, -l2s[rl]));
+          if (CAUSAL && key > i0 + rl) p = 0.f;
+          s[i] = p;
+          dp[i] = p * (dp[i] - dsm[rl]);
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS: step t carries query 16qb + 4g + t
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float* qr2 = qs + (16 * qb + 4 * g + t) * LD;
+          const float* or2 = os + (16 * qb + 4 * g + t) * LD;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dv[db] = mfma_f32(or2[16 * db + l16], s[t], dv[db]);
+            dk[db] = mfma_f32(qr2[16 * db + l16], dp[t], dk[db]);
+          }
+        }
+      }
+    }
+  }
+  if (key_ok) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      *reinterpret_cast<f32x4*>(dK + hoff + (size_t)key * D + 16 * db + 4 * g) = dk[db] * scale;
+      *reinterpret_cast<f32x4*>(dV + hoff + (size_t)key * D + 16 * db + 4 * g) = dv[db];
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512)
+void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                   const float* __restrict__ V, const float* __restrict__ dO,
+                   const float* __restrict__ LSE, const float* __restrict__ DELTA,
+                   float* __restrict__ dQ, int bh, int n, float scale, float scale_log2,
+                   int BR, int BC) {
+  extern __shared__ float smem[];
+  constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
+  const int BCP = (BC + 15) & ~15, nkb = BCP / 16;
+  float* ks = smem;
+  float* vs = smem + BCP * LD;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int ntq = (n + BR - 1) / BR;
+  const int head = blockIdx.x % bh;
+  const int q0 = (ntq - 1 - blockIdx.x / bh) * BR;
+  const int q0w = q0 + 16 * wave;
+  const int qr = q0w + l16;
+  const size_t hoff = (size_t)head * n * D;
+
+  float qf[NST], of[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    qf[st] = (qr < n) ? Q[hoff + (size_t)qr * D + 4 * st + g] : 0.f;
+    of[st] = (qr < n) ? dO[hoff + (size_t)qr * D + 4 * st + g] : 0.f;
+  }
+  const float l2q = (qr < n) ? LSE[(size_t)head * n + qr] * kLog2e : __builtin_inff();
+  const float dd = (qr < n) ? DELTA[(size_t)head * n + qr] : 0.f;
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kend = CAUSAL ? min(n, q0 + BR) : n;
+  const int ntk = (kend + BC - 1) / BC;
+  for (int j = 0; j < ntk; ++j) {
+    const int j0 = j * BC;
+    const int valid = min(BC, n - j0);
+    __syncthreads();
+    stage_f32_rows<D>(ks, K + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
+    stage_f32_rows<D>(vs, V + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
+    __syncthreads();
+    if (CAUSAL && j0 > q0w + 15) continue;
+#pragma unroll
+    for (int kb = 0; kb < kMaxBlk; ++kb) {
+      if (kb < nkb) {
+        // S^T and dP^T: lane holds key j0 + 16kb + 4g + i, query qr
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+        const float* krow = ks + (16 * kb + l16) * LD;
+        const float* vrow = vs + (16 * kb + l16) * LD;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          s = mfma_f32(krow[4 * st + g], qf[st], s);
+          dp = mfma_f32(vrow[4 * st + g], of[st], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kl = 16 * kb + 4 * g + i;
+          float p = exp2_fast(__builtin_fmaf(s[i], scale_log2, -l2q));
+          if (kl >= valid || (CAUSAL && j0 + kl > qr)) p = 0.f;
+          dp[i] = p * (dp[i] - dd);
+        }
+        // dQ^T += K^T dS^T: step t carries key 16kb + 4g + t
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float* kr2 = ks + (16 * kb + 4 * g + t) * LD;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma_f32(kr2[16 * db + l16], dp[t], acc[db]);
+        }
+      }
+    }
+  }
+  if (qr < n) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(dQ + hoff + (size_t)qr * D + 16 * db + 4 * g) = acc[db] * scale;
+  }
+}
+
+size_t f32_lds_bytes(int kernel, int d, int bm, int bn) {
+  const size_t ld = (size_t)d + 1;
+  const size_t bcp = (size_t)((bn + 15) & ~15);
+  if (kernel == 1) return (2 * (size_t)bm * ld + 2 * (size_t)bm) * sizeof(float);
+  return 2 * bcp * ld * sizeof(float);
+}
+
+template <typename KernelT>
+static hipError_t set_lds(KernelT kern, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+#define FA_F32_DISPATCH_D(MACRO) \
+  switch (d) {                   \
+    case 16: MACRO(16); break;   \
+    case 32: MACRO(32); break;   \
+    case 64: MACRO(64); break;   \
+    case 128: MACRO(128); break; \
+    default: return hipErrorInvalidValue; \
+  }
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int bh, int n, int d, float scale, int causal, int bm, int bn,
+                          hipStream_t st) {
+  const size_t lds = f32_lds_bytes(0, d, bm, bn);
+  const dim3 grid((unsigned)(((n + bm - 1) / bm) * bh)), block(bm * 4);
+  const float sl2 = scale * kLog2e;
+#define FA_FWD_F32(DD)                                                                      \
+  {                                                                                         \
+    auto kern = causal ? fwd_f32_kernel<DD, true> : fwd_f32_kernel<DD, false>;              \
+    hipError_t e = set_lds(kern, lds);                                                      \
+    if (e != hipSuccess) return e;                                                          \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, o, lse, bh, n, sl2, bm, bn);    \
+  }
+  FA_F32_DISPATCH_D(FA_FWD_F32)
+#undef FA_FWD_F32
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const float* dO,
+                           const float* lse, const float* delta, float* dk, float* dv,
+                           int bh, int n, int d, float scale, int causal, int bm, int bn,
+                           hipStream_t st) {
+  const size_t lds = f32_lds_bytes(1, d, bm, bn);
+  const dim3 grid((unsigned)(((n + bn - 1) / bn) * bh)), block(((bn + 15) / 16) * 64);
+  const float sl2 = scale * kLog2e;
+#define FA_DKDV_F32(DD)                                                                     \
+  {                                                                                         \
+    auto kern = causal ? dkdv_f32_kernel<DD, true> : dkdv_f32_kernel<DD, false>;            \
+    hipError_t e = set_lds(kern, lds);                                                      \
+    if (e != hipSuccess) return e;                                                          \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dk, dv, bh, n,  \
+                       scale, sl2, bm, bn);                                                 \
+  }
+  FA_F32_DISPATCH_D(FA_DKDV_F32)
+#undef FA_DKDV_F32
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_f32(const float* q, const float* k, const float* v, const float* dO,
+                         const float* lse, const float* delta, float* dq,
+                         int bh, int n, int d, float scale, int causal, int bm, int bn,
+                         hipStream_t st) {
+  const size_t lds = f32_lds_bytes(2, d, bm, bn);
+  const dim3 grid((unsigned)(((n + bm - 1) / bm) * bh)), block(bm * 4);
+  const float sl2 = scale * kLog2e;
+#define FA_DQ_F32(DD)                                                                       \
+  {                                                                                         \
+    auto kern = causal ? dq_f32_kernel<DD, true> : dq_f32_kernel<DD, false>;                \
+    hipError_t e = set_lds(kern, lds);                                                      \
+    if (e != hipSuccess) return e;                                                          \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dq, bh, n,      \
+                       scale, sl2, bm, bn);                                                 \
+  }
+  FA_F32_DISPATCH_D(FA_DQ_F32)
+#undef FA_DQ_F32
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_k O_ik dO_ik ("Assignment2 ... notes" section 1.4, Eq 17; the
+// identity of "CS349E lecture 11" demo1_gradcheck that needs one row of O and
+// dO only).  Each thread multiplies one 16-byte chunk of a row in fp32; the
+// lanes of a row are reduced with cross-lane adds.  HBM-bound streaming pass.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256)
+void preprocess_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                       float* __restrict__ delta, long long rows) {
+  constexpr int EPT = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  constexpr int LPR = D / EPT;                // lanes per row
+  constexpr int RPB = 256 / LPR;              // rows per block
+  static_assert(LPR >= 1 && LPR <= 64, "row must fit in a wave");
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = (threadIdx.x % LPR) * EPT;
+  float acc = 0.f;
+  if (row < rows) {
+    typedef T vec_t __attribute__((ext_vector_type(EPT)));
+    const vec_t o = *reinterpret_cast<const vec_t*>(O + row * D + c);
+    const vec_t g = *reinterpret_cast<const vec_t*>(dO + row * D + c);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && (threadIdx.x % LPR) == 0) delta[row] = acc;
+}
+
+template <typename T, int D>
+static hipError_t launch_pre_inst(const void* o, const void* dO, float* delta, long long rows,
+                                  hipStream_t st) {
+  constexpr int LPR = D / (16 / (int)sizeof(T));
+  constexpr int RPB = 256 / LPR;
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
+  hipLaunchKernelGGL((preprocess_kernel<T, D>), grid, block, 0, st, (const T*)o, (const T*)dO,
+                     delta, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_preprocess(const void* o, const void* dO, float* delta, int bh, int n, int d,
+                             int dtype, hipStream_t st) {
+  const long long rows = (long long)bh * n;
+  if (dtype == 0) {
+    switch (d) {
+      case 16: return launch_pre_inst<float, 16>(o, dO, delta, rows, st);
+      case 32: return launch_pre_inst<float, 32>(o, dO, delta, rows, st);
+      case 64: return launch_pre_inst<float, 64>(o, dO, delta, rows, st);
+      case 128: return launch_pre_inst<float, 128>(o, dO, delta, rows, st);
+    }
+  } else {
+    switch (d) {
+      case 64: return launch_pre_inst<__bf16, 64>(o, dO, delta, rows, st);
+      case 128: return launch_pre_inst<__bf16, 128>(o, dO, delta, rows, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

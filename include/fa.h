@@ -1,0 +1,127 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention library (libfa.so) for gfx950.
+ *
+ * The library computes exact attention O = softmax(scale * Q K^T) V and its
+ * gradients without ever forming the N x N score matrix:
+ *
+ *   fa_fwd             forward: Q in row tiles, K/V streamed in column tiles
+ *                      through an online softmax; saves only O and the
+ *                      per-row logsumexp L = m + ln(l).
+ *   fa_bwd_preprocess  D_i = sum_k dO_ik * O_ik, computed once before the
+ *                      backward proper.
+ *   fa_bwd_dkdv        dK, dV: outer loop over key/value tiles, P recomputed
+ *                      on chip as exp(S - L).
+ *   fa_bwd_dq          dQ: outer loop over query tiles, P recomputed again.
+ *
+ * Source of the method (cited by page and section):
+ *   "Assignment2: FlashAttention & Distributed Data Parallel notes"
+ *   (CS336), Part 1: section 1.2 (FA-2 forward: running max m, running sum l,
+ *   unnormalised accumulator, final O / l, saved L = m + log l), section 1.3
+ *   (one program per (batch, query tile); key tiles wholly above the
+ *   diagonal are skipped in causal mode), section 1.4 (Eq 13-19 and the
+ *   two-kernel backward that needs no atomics).
+ *   "CS349E lecture 11, 03_flash_backward.py" demo1_gradcheck (D from one row
+ *   of O and dO, computed before the backward), demo4_causal (only tiles
+ *   crossing the diagonal need an in-tile mask).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors.  q, k, v, o, dO, dq, dk, dv are contiguous row-major device
+ *   buffers of shape [bh][n][d] (bh = batch * heads; the head dimension d is
+ *   the fastest-moving index) holding elements of `dtype`.  lse (L) and
+ *   delta (D) are contiguous float32 device buffers of shape [bh][n].  Every
+ *   pointer must be 16-byte aligned.
+ * Math.  S = scale * Q K^T.  With causal != 0, key j is visible to query i
+ *   iff j <= i (top-left aligned, queries and keys both of length n); key
+ *   tiles with no visible key are skipped and only tiles crossing the
+ *   diagonal are masked.  L is the natural-log logsumexp of the scaled,
+ *   masked scores of each row.  Accumulation is float32; with FA_BF16 the
+ *   probabilities P and dS are rounded to bf16 (round to nearest even)
+ *   before they enter a bf16 matrix product, and outputs are rounded to
+ *   bf16 once at the end.  With FA_F32 every product is float32.
+ * n.  Any n >= 1 is accepted; a last tile shorter than the tile size is
+ *   masked (rows past n are neither read nor written).
+ * Tiles.  block_m (query rows per tile) and block_n (key columns per tile)
+ *   select the tiling; 0, 0 picks the library default.  FA_F32 accepts
+ *   block_m in {16, 32, 64, 128} and block_n in 4..128 (multiple of 4),
+ *   subject to the 160 KiB LDS budget.  FA_BF16 accepts only its tuned
+ *   tilings (0, 0 or the values fa_default_tiles reports).  The result does
+ *   not depend on the tiling beyond float rounding.
+ * Ownership.  The caller allocates and owns every buffer.  The library never
+ *   allocates, frees or synchronises, keeps no state between calls and is
+ *   safe to call from several host threads.  Outputs are fully overwritten
+ *   (never accumulated into) and must not alias any input.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *   only enqueues work on it and returns.  The caller orders
+ *   fa_bwd_preprocess before fa_bwd_dkdv and fa_bwd_dq (which are
+ *   independent of each other).
+ * Empty input.  bh == 0 or n == 0 is a no-op that returns FA_OK (pointers
+ *   are not touched and may be NULL).
+ * Errors.  Arguments are validated on the host before any HIP call; an
+ *   invalid call launches nothing and returns a non-zero status.  A launch
+ *   failure reported by the HIP runtime returns FA_ERR_HIP.  Faults during
+ *   execution surface at the caller's next synchronisation.  Nothing throws
+ *   or exits across this boundary.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad dtype/scale, aliasing */
+  FA_ERR_UNSUPPORTED = 2,   /* head dim, tiling or size not provided */
+  FA_ERR_MISALIGNED = 3,    /* a pointer is not 16-byte aligned */
+  FA_ERR_HIP = 4            /* the HIP runtime rejected a launch */
+} fa_status;
+
+/* Forward (CS336 notes 1.2-1.3).  Reads q, k, v; writes o [bh][n][d] and
+ * lse [bh][n] (float32, natural log). */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int bh, int n, int d, fa_dtype dtype, float scale, int causal,
+                 int block_m, int block_n, void* stream);
+
+/* Backward step 1 (CS336 notes 1.4 Eq 17, D = rowsum(O * dO)).  Reads o and
+ * dO; writes delta [bh][n] float32. */
+fa_status fa_bwd_preprocess(const void* o, const void* dO, float* delta,
+                            int bh, int n, int d, fa_dtype dtype, void* stream);
+
+/* Backward step 2 (CS336 notes 1.4 Eq 13-17, 15 and 19; the key/value-outer
+ * kernel).  Reads q, k, v, dO, lse (from fa_fwd with the same q, k, v, scale
+ * and causal) and delta (from fa_bwd_preprocess); writes dk and dv. */
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                      const float* lse, const float* delta, void* dk, void* dv,
+                      int bh, int n, int d, fa_dtype dtype, float scale, int causal,
+                      int block_m, int block_n, void* stream);
+
+/* Backward step 3 (CS336 notes 1.4 Eq 13-18; the query-outer kernel).
+ * Same inputs as fa_bwd_dkdv; writes dq. */
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                    const float* lse, const float* delta, void* dq,
+                    int bh, int n, int d, fa_dtype dtype, float scale, int causal,
+                    int block_m, int block_n, void* stream);
+
+/* The tiling (block_m, block_n) that block_m = block_n = 0 selects for a
+ * kernel (0 = fwd, 1 = dkdv, 2 = dq) at this dtype and head dim.  Returns
+ * FA_ERR_UNSUPPORTED for a head dim or dtype the library does not provide.  Pure
+ * host function. */
+fa_status fa_default_tiles(fa_dtype dtype, int d, int kernel, int* block_m, int* block_n);
+
+/* Static string for a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

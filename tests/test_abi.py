@@ -1,0 +1,170 @@
+"""C-ABI tests that need no GPU: libfa.so loads, exports every function that
+include/fa.h declares, and rejects invalid arguments on the host before any
+HIP call (so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_26_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 0x10000      # 16-byte aligned fake addresses (never dereferenced: calls are rejected first)
+B = 0x20000
+C = 0x30000
+D_ = 0x40000
+E = 0x50000
+F = 0x60000
+G = 0x70000
+H = 0x80000
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\**\s*(fa_[a-z0-9_]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert names == sorted(fa.SIGNATURES), names
+    for name in names:
+        assert hasattr(lib, name), name
+    # also check the dynamic symbol table directly
+    so = ctypes.CDLL(fa.LIB_PATH)
+    for name in names:
+        assert ctypes.cast(getattr(so, name), ctypes.c_void_p).value
+
+
+def test_version_and_strings(lib):
+    assert fa.fa_abi_version() == 1
+    for code in range(5):
+        assert fa.fa_status_str(code)
+    assert fa.fa_status_str(99) == "unknown status"
+
+
+def test_default_tiles(lib):
+    assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_FWD) == (128, 64)
+    assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_DKDV) == (64, 128)
+    assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_DQ) == (128, 64)
+    assert fa.fa_default_tiles(fa.FA_F32, 16, fa.KERNEL_FWD) == (64, 64)
+    with pytest.raises(fa.FAError):
+        fa.fa_default_tiles(fa.FA_BF16, 16, fa.KERNEL_FWD)
+    with pytest.raises(fa.FAError):
+        fa.fa_default_tiles(fa.FA_F32, 48, fa.KERNEL_FWD)
+    bm = ctypes.c_int()
+    assert lib.fa_default_tiles(0, 64, 7, ctypes.byref(bm), ctypes.byref(bm)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_default_tiles(0, 64, 0, None, None) == fa.FA_ERR_INVALID_ARG
+
+
+def fwd(lib, q=A, k=B, v=C, o=D_, lse=E, bh=1, n=64, d=64, dtype=fa.FA_BF16, scale=0.125, causal=1,
+        bm=0, bn=0):
+    return lib.fa_fwd(q, k, v, o, lse, bh, n, d, dtype, scale, causal, bm, bn, None)
+
+
+def dkdv(lib, **kw):
+    a = dict(q=A, k=B, v=C, dO=D_, lse=E, delta=F, dk=G, dv=H, bh=1, n=64, d=64, dtype=fa.FA_BF16,
+             scale=0.125, causal=1, bm=0, bn=0)
+    a.update(kw)
+    return lib.fa_bwd_dkdv(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dk"], a["dv"],
+                           a["bh"], a["n"], a["d"], a["dtype"], a["scale"], a["causal"], a["bm"], a["bn"], None)
+
+
+def dq(lib, **kw):
+    a = dict(q=A, k=B, v=C, dO=D_, lse=E, delta=F, dq=G, bh=1, n=64, d=64, dtype=fa.FA_BF16,
+             scale=0.125, causal=1, bm=0, bn=0)
+    a.update(kw)
+    return lib.fa_bwd_dq(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dq"],
+                         a["bh"], a["n"], a["d"], a["dtype"], a["scale"], a["causal"], a["bm"], a["bn"], None)
+
+
+def test_null_pointers_rejected(lib):
+    assert fwd(lib, q=0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(lib, lse=0) == fa.FA_ERR_INVALID_ARG
+    assert dkdv(lib, delta=0) == fa.FA_ERR_INVALID_ARG
+    assert dq(lib, dq=0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_preprocess(A, 0, C, 1, 64, 64, fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_misaligned_rejected(lib):
+    assert fwd(lib, k=B + 2) == fa.FA_ERR_MISALIGNED
+    assert fwd(lib, lse=E + 4) == fa.FA_ERR_MISALIGNED
+    assert dkdv(lib, dv=H + 8) == fa.FA_ERR_MISALIGNED
+    assert dq(lib, dO=D_ + 2) == fa.FA_ERR_MISALIGNED
+    assert lib.fa_bwd_preprocess(A + 2, B, C, 1, 64, 64, fa.FA_BF16, None) == fa.FA_ERR_MISALIGNED
+
+
+def test_sizes_and_dtypes(lib):
+    assert fwd(lib, n=-1) == fa.FA_ERR_INVALID_ARG
+    assert fwd(lib, bh=-3) == fa.FA_ERR_INVALID_ARG
+    assert fwd(lib, d=0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(lib, dtype=7) == fa.FA_ERR_INVALID_ARG
+    assert fwd(lib, d=48) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, d=16, dtype=fa.FA_BF16) == fa.FA_ERR_UNSUPPORTED   # bf16 provides d = 64, 128
+    assert fwd(lib, n=(1 << 24) + 1) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, bh=(1 << 20) + 1) == fa.FA_ERR_UNSUPPORTED
+    assert dkdv(lib, d=256) == fa.FA_ERR_UNSUPPORTED
+    assert dq(lib, d=32, dtype=fa.FA_BF16) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_grid_limit(lib):
+    # float32 dK/dV with 4-key tiles at the largest n and bh would exceed 2^31 workgroups
+    assert dkdv(lib, dtype=fa.FA_F32, d=16, bm=16, bn=4, n=1 << 24, bh=1 << 10) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_scale_must_be_finite_positive(lib):
+    for s in (float("nan"), float("inf"), 0.0, -0.5):
+        assert fwd(lib, scale=s) == fa.FA_ERR_INVALID_ARG
+        assert dkdv(lib, scale=s) == fa.FA_ERR_INVALID_ARG
+        assert dq(lib, scale=s) == fa.FA_ERR_INVALID_ARG
+
+
+def test_tilings(lib):
+    # bf16: only the tuned tilings
+    assert fwd(lib, bm=64, bn=64, q=0) == fa.FA_ERR_UNSUPPORTED    # tiling is checked before pointers
+    assert dkdv(lib, bm=128, bn=128, q=0) == fa.FA_ERR_UNSUPPORTED
+    assert dq(lib, bm=16, bn=16, q=0) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, bm=-1, bn=0) == fa.FA_ERR_INVALID_ARG
+    # float32: block_m in {16,32,64,128}, block_n multiple of 4 up to 128, LDS budget
+    f32 = dict(dtype=fa.FA_F32, d=16, q=0)
+    assert fwd(lib, bm=16, bn=12, **f32) == fa.FA_ERR_INVALID_ARG           # accepted tiling, then null q
+    assert fwd(lib, bm=48, bn=16, **f32) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, bm=16, bn=14, **f32) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, bm=16, bn=132, **f32) == fa.FA_ERR_UNSUPPORTED
+    assert dkdv(lib, bm=128, bn=128, dtype=fa.FA_F32, d=128, q=0) == fa.FA_ERR_INVALID_ARG  # 129 KiB fits
+    for bm, bn in ((16, 12), (16, 16), (32, 64), (64, 32), (128, 128)):
+        assert dq(lib, bm=bm, bn=bn, dtype=fa.FA_F32, d=32, q=0) == fa.FA_ERR_INVALID_ARG
+
+
+def test_empty_input_is_noop(lib):
+    # bh == 0 or n == 0: nothing to do, pointers are not touched
+    assert fwd(lib, q=0, k=0, v=0, o=0, lse=0, bh=0) == fa.FA_OK
+    assert fwd(lib, q=0, k=0, v=0, o=0, lse=0, n=0) == fa.FA_OK
+    assert dkdv(lib, q=0, dk=0, n=0) == fa.FA_OK
+    assert dq(lib, q=0, dq=0, bh=0) == fa.FA_OK
+    assert lib.fa_bwd_preprocess(0, 0, 0, 0, 64, 64, fa.FA_BF16, None) == fa.FA_OK
+
+
+def test_outputs_must_not_alias(lib):
+    assert fwd(lib, o=A) == fa.FA_ERR_INVALID_ARG
+    assert fwd(lib, lse=D_) == fa.FA_ERR_INVALID_ARG
+    assert dkdv(lib, dk=H) == fa.FA_ERR_INVALID_ARG
+    assert dkdv(lib, dv=B) == fa.FA_ERR_INVALID_ARG
+    assert dq(lib, dq=F) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_preprocess(A, B, A, 1, 64, 64, fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q, causal=True)
