@@ -51,6 +51,39 @@ def kernel_bytes(bh, n, d, elt):
     return {"fwd": 4 * t + r, "preprocess": 2 * t + r, "dkdv": 6 * t + 2 * r, "dq": 5 * t + 2 * r}
 
 
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "attention_kernels_headline_8192_d128_causal_bf16.md")
+KERNEL_SOURCES = {
+    "fwd": ("fa_fwd_bf16.hip", "fa_common.h"),
+    "dkdv": ("fa_bwd_bf16.hip", "fa_common.h"),
+    "dq": ("fa_bwd_bf16.hip", "fa_common.h"),
+    "preprocess": ("fa_f32.hip",),
+}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_tiled_attention_26_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (headline workload, default tilings), or None when the kernel's sources
+    have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_TABLE) as fh:
+            for line in fh:
+                cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                if len(cells) >= 5 and cells[0] == kernel and cells[1] == source_hash(kernel):
+                    return int(cells[4])
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(bh, n, d, causal, budget_s=25.0):
     """The fp64 oracle timed on host cores on a bounded sample of the same
     workload: whole heads (forward + backward) until about `budget_s`."""
@@ -89,6 +122,32 @@ def cpu_baseline(bh, n, d, causal, budget_s=25.0):
     }
 
 
+def rocprof_summary(paths):
+    """Print a short text summary of rocprofv3 result databases (rocpd
+    SQLite): per-kernel dispatch count and duration statistics from a
+    --kernel-trace run, per-kernel counter averages from a --pmc run."""
+    import sqlite3
+    for path in paths:
+        con = sqlite3.connect(path)
+        print(f"## {os.path.basename(os.path.dirname(path))}/{os.path.basename(path)}")
+        rows = con.execute(
+            "select name, count(*), avg(end - start), min(end - start), max(end - start) "
+            "from kernels group by name order by sum(end - start) desc").fetchall()
+        if rows:
+            print(f"{'calls':>5} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel")
+            for name, cnt, avg, mn, mx in rows:
+                print(f"{cnt:5d} {avg / 1e3:10.1f} {mn / 1e3:10.1f} {mx / 1e3:10.1f}  {name[:100]}")
+        try:
+            pm = con.execute("select name, counter_name, avg(counter_value), count(*) from pmc_events "
+                             "group by name, counter_name order by name").fetchall()
+        except sqlite3.OperationalError:
+            pm = []
+        if pm:
+            print(f"{'counter':>12} {'avg_KiB':>14} {'dispatches':>10}  kernel")
+            for name, cn, val, cnt in pm:
+                print(f"{cn:>12} {val:14.1f} {cnt:10d}  {name[:100]}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,7 +160,15 @@ def main():
     ap.add_argument("--fwd-tiles", default="0,0")
     ap.add_argument("--dkdv-tiles", default="0,0")
     ap.add_argument("--dq-tiles", default="0,0")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times); used to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="DB",
+                    help="only print a text summary of rocprofv3 result databases")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -113,6 +180,16 @@ def main():
 
     import exact_tiled_attention_26_amd as fa
     from workloads import WORKLOADS, cast_io, make_inputs
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 3}))
+        return
 
     w = WORKLOADS[args.workload]
     causal = not args.non_causal
@@ -190,7 +267,10 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": None,
+        "traffic": (measured_traffic(dom)
+                    if (w.name == "headline_8192_d128" and causal and ft == (0, 0) and kt == (0, 0)
+                        and qt == (0, 0)) else None),
+        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
         "avg_launch_ms": round(avg[dom], 4),
         "algorithmic_flops_per_launch": kfl[dom],
     }

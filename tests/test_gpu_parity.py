@@ -42,9 +42,23 @@ def run_gpu(arrays, dtype, causal, fwd_tiles=(0, 0), dkdv_tiles=(0, 0), dq_tiles
     return out
 
 
-def compare_full(g, dtype, causal, scale=None, label=""):
-    """Whole-tensor comparison with the oracle; returns the error report."""
-    tol = TOL[dtype]
+def _rel(err, ref):
+    """Gradient error relative to max |ref|.  Where the exact gradient is 0
+    (a single token: dQ = dK = 0) the error is taken relative to 1."""
+    return err / max(np.abs(ref).max(), 1.0 if np.abs(ref).max() == 0 else 0.0)
+
+
+def compare_full(g, dtype, causal, scale=None, label="", magnitude=1.0):
+    """Whole-tensor comparison with the oracle; returns the error report.
+
+    `magnitude` widens the O and L bounds for inputs whose scores are far
+    larger than the N(0, 1) workloads': an fp32 logsumexp of size |L| cannot
+    be closer than about |L| * 2^-24, so the bounds there are taken relative
+    to the score scale.
+    """
+    tol = dict(TOL[dtype])
+    tol["o"] *= magnitude
+    tol["lse"] *= magnitude
     o_ref, l_ref = oracle.attention_forward(g["q"], g["k"], g["v"], scale=scale, causal=causal)
     dq_ref, dk_ref, dv_ref, _ = oracle.attention_backward(g["q"], g["k"], g["v"], g["do"], scale=scale,
                                                           causal=causal)
@@ -54,9 +68,9 @@ def compare_full(g, dtype, causal, scale=None, label=""):
         "o": np.abs(g["o"] - o_ref).max(),
         "lse": np.abs(g["lse"] - l_ref).max(),
         "delta": np.abs(g["delta"] - d_ref).max() / max(1.0, np.abs(d_ref).max()),
-        "dq": np.abs(g["dq"] - dq_ref).max() / np.abs(dq_ref).max(),
-        "dk": np.abs(g["dk"] - dk_ref).max() / np.abs(dk_ref).max(),
-        "dv": np.abs(g["dv"] - dv_ref).max() / np.abs(dv_ref).max(),
+        "dq": _rel(np.abs(g["dq"] - dq_ref).max(), dq_ref),
+        "dk": _rel(np.abs(g["dk"] - dk_ref).max(), dk_ref),
+        "dv": _rel(np.abs(g["dv"] - dv_ref).max(), dv_ref),
     }
     _say(f"[{label}] " + " ".join(f"{k}={v:.2e}" for k, v in rep.items()))
     assert rep["o"] <= tol["o"], rep
@@ -140,11 +154,15 @@ def test_ragged_bf16(d, n, causal):
 
 @pytest.mark.parametrize("dtype,d", [("fp32", 32), ("bf16", 128)])
 def test_large_scores_stay_finite(dtype, d):
-    """Scores of order 1e2-1e3 (Q scaled by 50): the online softmax never
-    overflows and still matches the oracle."""
+    """Scores of order 1e2 (Q scaled by 50): the online softmax never
+    overflows and still matches the oracle.  The O and L bounds scale with the
+    largest |score| / 10 (L ~ 200 here; fp32 resolves it to ~1e-5)."""
     q, k, v, do = make_inputs(2, 300, d, seed=5)
-    g = run_gpu((q * 50, k, v, do), dtype, True)
-    compare_full(g, dtype, True, label=f"{dtype} large scores")
+    q = q * 50
+    g = run_gpu((q, k, v, do), dtype, True)
+    smax = max(np.abs(g["q"][h] @ g["k"][h].T).max() / np.sqrt(d) for h in range(2))
+    compare_full(g, dtype, True, label=f"{dtype} large scores (max |S| {smax:.0f})",
+                 magnitude=max(1.0, smax / 10))
 
 
 def test_explicit_scale_fp32():
