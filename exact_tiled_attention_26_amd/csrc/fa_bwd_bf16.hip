@@ -28,38 +28,39 @@
 
 namespace fa {
 
-// Stage BR floats of L (converted to base 2) and D for rows [i0, i0 + BR).
-// Rows past n get L = +inf (so P = 0) and D = 0.
+// Asynchronous copy of BR consecutive fp32 row values (L or D) of one head
+// into LDS with global_load_lds_dword (lane i -> LDS float i).  Rows at or past
+// n re-read row n - 1; the kernels mask those rows.
 template <int BR>
-__device__ __forceinline__ void stage_rows(const float* lse, const float* delta, int i0, int n,
-                                           float* l2_dst, float* d_dst, int tid) {
-  if (tid < BR) {
-    const int r = i0 + tid;
-    l2_dst[tid] = (r < n) ? lse[r] * kLog2e : __builtin_inff();
-    d_dst[tid] = (r < n) ? delta[r] : 0.f;
+__device__ __forceinline__ void rows_load_async(float* lds, const float* src, int i0, int n,
+                                                int lane) {
+  static_assert(BR % 64 == 0, "one dword per lane");
+#pragma unroll
+  for (int k = 0; k < BR / 64; ++k) {
+    const int r = min(i0 + 64 * k + lane, n - 1);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + r),
+                                     (__attribute__((address_space(3))) void*)(lds + 64 * k), 4, 0, 0);
   }
 }
 
 template <int D, int KW, int NW, int BR, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, (KW >= 32 ? 1 : 2))
+__global__ __launch_bounds__(NW * 64, 1)
 void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ DELTA,
                       __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                       int bh, int n, float scale, float scale_log2) {
   constexpr int BC = KW * NW;
-  constexpr int NT = NW * 64;
   constexpr int NKB = KW / 16;   // 16-key blocks per wave
-  constexpr int NQB = BR / 16;   // 16-query blocks per query tile
   constexpr int NDS = D / 32;
   constexpr int NDB = D / 16;
-  constexpr int NQS = BR / 32;   // 32-query steps (dV, dK contractions)
-  static_assert(BR <= NT, "row staging needs one thread per row");
+  constexpr int NQS = BR / 32;   // 32-query steps per query tile
+  static_assert(NW >= 2, "two waves stage the row values");
 
-  __shared__ __bf16 q_lds[2][BR * D];
-  __shared__ __bf16 do_lds[2][BR * D];
-  __shared__ float l2_lds[2][BR];
-  __shared__ float d_lds[2][BR];
+  __shared__ __bf16 q_lds0[BR * D], q_lds1[BR * D];
+  __shared__ __bf16 o_lds0[BR * D], o_lds1[BR * D];
+  __shared__ float l_lds0[BR], l_lds1[BR];
+  __shared__ float d_lds0[BR], d_lds1[BR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -73,6 +74,17 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const __bf16* dOh = dO + hoff;
   const float* Lh = LSE + (size_t)head * n;
   const float* Dh = DELTA + (size_t)head * n;
+
+  const int ntq = (n + BR - 1) / BR;
+  const int it0 = CAUSAL ? (k0 / BR) : 0;   // earlier query rows see none of these keys
+  const AsyncTileCopy<D, BR, NW> copier(wave, lane);
+  auto issue_tile = [&](__bf16* qd, __bf16* od, float* ld, float* dd, int i0) __attribute__((always_inline)) {
+    copier.issue(qd, Qh + (size_t)i0 * D, n - i0);
+    copier.issue(od, dOh + (size_t)i0 * D, n - i0);
+    if (wave == 0) rows_load_async<BR>(ld, Lh, i0, n, lane);
+    if (wave == 1) rows_load_async<BR>(dd, Dh, i0, n, lane);
+  };
+  issue_tile(q_lds0, o_lds0, l_lds0, d_lds0, it0 * BR);
 
   // K and V rows of this wave as B operands: lane holds row k0w + 16kb + l16,
   // columns 32ds + 8g .. +7.
@@ -102,111 +114,139 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       dv[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  const int ntq = (n + BR - 1) / BR;
-  const int it0 = CAUSAL ? (k0 / BR) : 0;   // earlier query rows see none of these keys
-
-  TileCopy<D, BR, NT> qc, oc;
-  {
-    const int i0 = it0 * BR;
-    qc.load(Qh + (size_t)i0 * D, n - i0, tid);
-    oc.load(dOh + (size_t)i0 * D, n - i0, tid);
-    qc.store(q_lds[0], tid);
-    oc.store(do_lds[0], tid);
-    stage_rows<BR>(Lh, Dh, i0, n, l2_lds[0], d_lds[0], tid);
-  }
+  const NatReader<D> nat(l16, g);
+  const TrReader<D> tr(l16, g);
+  async_copy_wait();
   __syncthreads();
 
-  for (int it = it0; it < ntq; ++it) {
-    const int i0 = it * BR;
-    const int buf = (it - it0) & 1;
-    const bool more = it + 1 < ntq;
-    float l2_next = 0.f, d_next = 0.f;
-    if (more) {
-      qc.load(Qh + (size_t)(i0 + BR) * D, n - i0 - BR, tid);
-      oc.load(dOh + (size_t)(i0 + BR) * D, n - i0 - BR, tid);
-      if (tid < BR) {
-        const int r = i0 + BR + tid;
-        l2_next = (r < n) ? Lh[r] * kLog2e : __builtin_inff();
-        d_next = (r < n) ? Dh[r] : 0.f;
+  // Stages of one 32-query step t of a query tile (software-pipelined below:
+  // the S/dP products of step t+1 are issued while the VALU turns step t into
+  // P and dS, so the matrix cores are not idle during the softmax work).
+  using Acc = f32x4[2][NKB];
+  auto stage_sdp = [&](const __bf16* qt, const __bf16* ot, int t, Acc& s, Acc& dp) __attribute__((always_inline)) {
+    // S = Q K^T and dP = dO V^T: lane holds query 32t + 16h + 4g + i, key 16kb + l16.
+    // Operands are read PF steps ahead of their MFMAs (see the dQ kernel).
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    constexpr int PF = 3, U = NDS * 2;             // steps: (ds, h)
+    bf16x8 qa[PF], oa[PF];
+#pragma unroll
+    for (int u = 0; u < PF && u < U; ++u) {
+      qa[u] = nat.read(qt, 32 * t + 16 * (u & 1), u >> 1);
+      oa[u] = nat.read(ot, 32 * t + 16 * (u & 1), u >> 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ds = u >> 1, h = u & 1;
+      const bf16x8 aq = qa[u % PF], ao = oa[u % PF];
+      if (u + PF < U) {
+        qa[u % PF] = nat.read(qt, 32 * t + 16 * ((u + PF) & 1), (u + PF) >> 1);
+        oa[u % PF] = nat.read(ot, 32 * t + 16 * ((u + PF) & 1), (u + PF) >> 1);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[h][kb] = mfma_bf16(aq, kf[kb][ds], s[h][kb]);
+        dp[h][kb] = mfma_bf16(ao, vf[kb][ds], dp[h][kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // P = exp(S - L) (Eq 14) and dS = P (dP - D) (Eq 17), packed to bf16 operands
+  auto stage_pds = [&](const float* lt, const float* dt, int i0, int t, bool need_mask,
+                       const Acc& s, const Acc& dp, bf16x8 (&pb)[NKB], bf16x8 (&sb)[NKB]) __attribute__((always_inline)) {
+    f32x4 pv[2][NKB], dv4[2][NKB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rl = 32 * t + 16 * h + 4 * g;     // first of this lane's 4 rows
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rl);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rl);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float l2 = l4[i] * kLog2e;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          float p = exp2_fast(__builtin_fmaf(s[h][kb][i], scale_log2, -l2));
+          if (need_mask) {
+            const int q = i0 + rl + i;
+            if ((CAUSAL && k0w + 16 * kb + l16 > q) || q >= n) p = 0.f;
+          }
+          pv[h][kb][i] = p;
+          dv4[h][kb][i] = p * (dp[h][kb][i] - d4[i]);
+        }
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      pb[kb] = pack_bf16(pv[0][kb], pv[1][kb]);
+      sb[kb] = pack_bf16(dv4[0][kb], dv4[1][kb]);
+    }
+  };
+  // dV^T += dO^T P (Eq 15) and dK^T += Q^T dS (Eq 19, scale applied at the end)
+  auto stage_dvdk = [&](const __bf16* qt, const __bf16* ot, int t, const bf16x8 (&pb)[NKB],
+                        const bf16x8 (&sb)[NKB]) __attribute__((always_inline)) {
+    constexpr int PF = 3, U = NDB;                 // steps: db
+    bf16x8 oa[PF], qa[PF];
+#pragma unroll
+    for (int u = 0; u < PF && u < U; ++u) {
+      oa[u] = cat(tr.read(ot, 32 * t, u), tr.read(ot, 32 * t + 16, u));
+      qa[u] = cat(tr.read(qt, 32 * t, u), tr.read(qt, 32 * t + 16, u));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bf16x8 ao = oa[u % PF], aq = qa[u % PF];
+      if (u + PF < U) {
+        oa[u % PF] = cat(tr.read(ot, 32 * t, u + PF), tr.read(ot, 32 * t + 16, u + PF));
+        qa[u % PF] = cat(tr.read(qt, 32 * t, u + PF), tr.read(qt, 32 * t + 16, u + PF));
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        dv[u][kb] = mfma_bf16(ao, pb[kb], dv[u][kb]);
+        dk[u][kb] = mfma_bf16(aq, sb[kb], dk[u][kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The steps of a tile run as a three-stage software pipeline: dV/dK of
+  // step t-1, then P/dS of step t, then S/dP of step t+1 (independent work
+  // back to back, so MFMAs still in flight overlap the VALU stage).
+  auto pipelined = [&](const __bf16* qt, const __bf16* ot, const float* lt, const float* dt,
+                       int i0, bool need_mask) __attribute__((always_inline)) {
+    Acc sa[2], pa[2];
+    bf16x8 pbuf[2][NKB], sbuf[2][NKB];
+    stage_sdp(qt, ot, 0, sa[0], pa[0]);
+#pragma unroll
+    for (int t = 0; t < NQS; ++t) {
+      if (t >= 1) stage_dvdk(qt, ot, t - 1, pbuf[(t - 1) & 1], sbuf[(t - 1) & 1]);
+      stage_pds(lt, dt, i0, t, need_mask, sa[t & 1], pa[t & 1], pbuf[t & 1], sbuf[t & 1]);
+      if (t + 1 < NQS) stage_sdp(qt, ot, t + 1, sa[(t + 1) & 1], pa[(t + 1) & 1]);
+    }
+    stage_dvdk(qt, ot, NQS - 1, pbuf[(NQS - 1) & 1], sbuf[(NQS - 1) & 1]);
+  };
+
+  auto tile_step = [&](const __bf16* qt, const __bf16* ot, const float* lt, const float* dt,
+                       __bf16* qn, __bf16* on, float* ln, float* dn, int it) __attribute__((always_inline)) {
+    const int i0 = it * BR;
+    if (it + 1 < ntq) issue_tile(qn, on, ln, dn, i0 + BR);
     const bool active = !CAUSAL || (i0 + BR - 1 >= k0w);
     if (active) {
-      const __bf16* qt = q_lds[buf];
-      const __bf16* ot = do_lds[buf];
-      const float* l2t = l2_lds[buf];
-      const float* dt = d_lds[buf];
-      // S = Q K^T and dP = dO V^T: lane holds query 16qb + 4g + i, key 16kb + l16
-      f32x4 s[NQB][NKB], dp[NQB][NKB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const bf16x8 aq = lds_read_chunk<D>(qt, 16 * qb + l16, 4 * ds + g);
-          const bf16x8 ao = lds_read_chunk<D>(ot, 16 * qb + l16, 4 * ds + g);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            s[qb][kb] = mfma_bf16(aq, kf[kb][ds], s[qb][kb]);
-            dp[qb][kb] = mfma_bf16(ao, vf[kb][ds], dp[qb][kb]);
-          }
-        }
-      }
-      // P = exp(S - L) (Eq 14) and dS = P (dP - D) (Eq 17)
-      const bool need_mask = CAUSAL && (i0 < k0w + KW - 1);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rl = 16 * qb + 4 * g + i;
-          const float l2 = l2t[rl];
-          const float dd = dt[rl];
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            float p = exp2_fast(__builtin_fmaf(s[qb][kb][i], scale_log2, -l2));
-            if (need_mask && (k0w + 16 * kb + l16 > i0 + rl)) p = 0.f;
-            s[qb][kb][i] = p;
-            dp[qb][kb][i] = p * (dp[qb][kb][i] - dd);
-          }
-        }
-      // dV^T += dO^T P (Eq 15) and dK^T += Q^T dS (Eq 19, scale applied at the end)
-#pragma unroll
-      for (int t = 0; t < NQS; ++t) {
-        bf16x8 pb[NKB], sb[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          pb[kb] = pack_bf16(s[2 * t][kb], s[2 * t + 1][kb]);
-          sb[kb] = pack_bf16(dp[2 * t][kb], dp[2 * t + 1][kb]);
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 ao = cat(lds_read_tr4<D>(ot, 32 * t + 4 * g, 16 * db, l16),
-                                lds_read_tr4<D>(ot, 32 * t + 16 + 4 * g, 16 * db, l16));
-          const bf16x8 aq = cat(lds_read_tr4<D>(qt, 32 * t + 4 * g, 16 * db, l16),
-                                lds_read_tr4<D>(qt, 32 * t + 16 + 4 * g, 16 * db, l16));
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            dv[db][kb] = mfma_bf16(ao, pb[kb], dv[db][kb]);
-            dk[db][kb] = mfma_bf16(aq, sb[kb], dk[db][kb]);
-          }
-        }
-      }
+      // only tiles crossing the diagonal or the end of the sequence are masked
+      pipelined(qt, ot, lt, dt, i0, (CAUSAL && i0 < k0w + KW - 1) || (i0 + BR > n));
     }
-    if (more) {
-      qc.store(q_lds[buf ^ 1], tid);
-      oc.store(do_lds[buf ^ 1], tid);
-      if (tid < BR) {
-        l2_lds[buf ^ 1][tid] = l2_next;
-        d_lds[buf ^ 1][tid] = d_next;
-      }
-    }
+    async_copy_wait();
     __syncthreads();
+  };
+
+  for (int it = it0; it < ntq; it += 2) {
+    tile_step(q_lds0, o_lds0, l_lds0, d_lds0, q_lds1, o_lds1, l_lds1, d_lds1, it);
+    if (it + 1 < ntq) tile_step(q_lds1, o_lds1, l_lds1, d_lds1, q_lds0, o_lds0, l_lds0, d_lds0, it + 1);
   }
 
   // write dK = scale * dK_acc and dV
@@ -230,21 +270,20 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 }
 
 template <int D, int QW, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, (QW * D >= 4096 ? 1 : 2))
+__global__ __launch_bounds__(NW * 64, 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                     const float* __restrict__ LSE, const float* __restrict__ DELTA,
                     __bf16* __restrict__ dQ, int bh, int n, float scale, float scale_log2) {
   constexpr int BR = QW * NW;
-  constexpr int NT = NW * 64;
   constexpr int NQB = QW / 16;
   constexpr int NKB = BC / 16;
   constexpr int NDS = D / 32;
   constexpr int NDB = D / 16;
   constexpr int NKS = BC / 32;
 
-  __shared__ __bf16 k_lds[2][BC * D];
-  __shared__ __bf16 v_lds[2][BC * D];
+  __shared__ __bf16 k_lds0[BC * D], k_lds1[BC * D];
+  __shared__ __bf16 v_lds0[BC * D], v_lds1[BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -257,6 +296,12 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const size_t hoff = (size_t)head * n * D;
   const __bf16* Kh = K + hoff;
   const __bf16* Vh = V + hoff;
+
+  const int kend = CAUSAL ? min(n, q0 + BR) : n;
+  const int ntk = (kend + BC - 1) / BC;
+  const AsyncTileCopy<D, BC, NW> copier(wave, lane);
+  copier.issue(k_lds0, Kh, min(BC, n));
+  copier.issue(v_lds0, Vh, min(BC, n));
 
   bf16x8 qf[NQB][NDS], of[NQB][NDS];
   float l2q[NQB], dq_d[NQB];
@@ -284,28 +329,19 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int kend = CAUSAL ? min(n, q0 + BR) : n;
-  const int ntk = (kend + BC - 1) / BC;
-
-  TileCopy<D, BC, NT> kc, vc;
-  kc.load(Kh, n, tid);
-  vc.load(Vh, n, tid);
-  kc.store(k_lds[0], tid);
-  vc.store(v_lds[0], tid);
+  const NatReader<D> nat(l16, g);
+  const TrReader<D> tr(l16, g);
+  async_copy_wait();
   __syncthreads();
 
-  for (int j = 0; j < ntk; ++j) {
+  auto tile_step = [&](const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn, int j) __attribute__((always_inline)) {
     const int j0 = j * BC;
-    const int buf = j & 1;
-    const bool more = j + 1 < ntk;
-    if (more) {
-      kc.load(Kh + (size_t)(j0 + BC) * D, n - j0 - BC, tid);
-      vc.load(Vh + (size_t)(j0 + BC) * D, n - j0 - BC, tid);
+    if (j + 1 < ntk) {
+      copier.issue(kn, Kh + (size_t)(j0 + BC) * D, n - j0 - BC);
+      copier.issue(vn, Vh + (size_t)(j0 + BC) * D, n - j0 - BC);
     }
     const bool active = !CAUSAL || (j0 <= q0w + QW - 1);
     if (active) {
-      const __bf16* kt = k_lds[buf];
-      const __bf16* vt = v_lds[buf];
       // S^T = K Q^T, dP^T = V dO^T: lane holds key 16kb + 4g + i, query 16qb + l16
       f32x4 s[NKB][NQB], dp[NKB][NQB];
 #pragma unroll
@@ -315,53 +351,79 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+      // operands are read PF steps ahead of the MFMAs that use them; the
+      // scheduling fences keep each read where it was issued, so LDS latency
+      // hides behind the matrix work instead of stalling it
+      constexpr int PF = 3;
+      constexpr int U1 = NDS * NKB;                // steps of S^T / dP^T: (ds, kb)
+      bf16x8 ka[PF], va[PF];
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
+      for (int u = 0; u < PF && u < U1; ++u) {
+        ka[u] = nat.read(kt, 16 * (u % NKB), u / NKB);
+        va[u] = nat.read(vt, 16 * (u % NKB), u / NKB);
+      }
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 ak = lds_read_chunk<D>(kt, 16 * kb + l16, 4 * ds + g);
-          const bf16x8 av = lds_read_chunk<D>(vt, 16 * kb + l16, 4 * ds + g);
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            s[kb][qb] = mfma_bf16(ak, qf[qb][ds], s[kb][qb]);
-            dp[kb][qb] = mfma_bf16(av, of[qb][ds], dp[kb][qb]);
-          }
+      for (int u = 0; u < U1; ++u) {
+        const int ds = u / NKB, kb = u % NKB;
+        const bf16x8 ak = ka[u % PF], av = va[u % PF];
+        if (u + PF < U1) {
+          ka[u % PF] = nat.read(kt, 16 * ((u + PF) % NKB), (u + PF) / NKB);
+          va[u % PF] = nat.read(vt, 16 * ((u + PF) % NKB), (u + PF) / NKB);
         }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          s[kb][qb] = mfma_bf16(ak, qf[qb][ds], s[kb][qb]);
+          dp[kb][qb] = mfma_bf16(av, of[qb][ds], dp[kb][qb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       const bool need_mask = (CAUSAL && j0 + BC - 1 > q0w) || (j0 + BC > n);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int last = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
+        const int lim = last - j0 - 4 * g;     // key j0 + 16kb + 4g + i visible iff 16kb + i <= lim
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float p = exp2_fast(__builtin_fmaf(s[kb][qb][i], scale_log2, -l2q[qb]));
-            if (need_mask) {
-              const int key = j0 + 16 * kb + 4 * g + i;
-              if ((CAUSAL && key > q0w + 16 * qb + l16) || key >= n) p = 0.f;
-            }
+            if (need_mask && 16 * kb + i > lim) p = 0.f;
             dp[kb][qb][i] = p * (dp[kb][qb][i] - dq_d[qb]);
           }
+      }
       // dQ^T += K^T dS^T (Eq 18, scale applied at the end)
+      bf16x8 sb[NKS][NQB];
 #pragma unroll
-      for (int t = 0; t < NKS; ++t) {
-        bf16x8 sb[NQB];
+      for (int t = 0; t < NKS; ++t)
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) sb[qb] = pack_bf16(dp[2 * t][qb], dp[2 * t + 1][qb]);
+        for (int qb = 0; qb < NQB; ++qb) sb[t][qb] = pack_bf16(dp[2 * t][qb], dp[2 * t + 1][qb]);
+      constexpr int PF3 = 4;
+      constexpr int U3 = NKS * NDB;                // steps: (t, db)
+      bf16x8 ta[PF3];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = cat(lds_read_tr4<D>(kt, 32 * t + 4 * g, 16 * db, l16),
-                               lds_read_tr4<D>(kt, 32 * t + 16 + 4 * g, 16 * db, l16));
+      for (int u = 0; u < PF3 && u < U3; ++u)
+        ta[u] = cat(tr.read(kt, 32 * (u / NDB), u % NDB), tr.read(kt, 32 * (u / NDB) + 16, u % NDB));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) acc[db][qb] = mfma_bf16(a, sb[qb], acc[db][qb]);
+      for (int u = 0; u < U3; ++u) {
+        const int t = u / NDB, db = u % NDB;
+        const bf16x8 a = ta[u % PF3];
+        if (u + PF3 < U3) {
+          const int t2 = (u + PF3) / NDB, db2 = (u + PF3) % NDB;
+          ta[u % PF3] = cat(tr.read(kt, 32 * t2, db2), tr.read(kt, 32 * t2 + 16, db2));
         }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) acc[db][qb] = mfma_bf16(a, sb[t][qb], acc[db][qb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (more) {
-      kc.store(k_lds[buf ^ 1], tid);
-      vc.store(v_lds[buf ^ 1], tid);
-    }
+    async_copy_wait();
     __syncthreads();
+  };
+
+  for (int j = 0; j < ntk; j += 2) {
+    tile_step(k_lds0, v_lds0, k_lds1, v_lds1, j);
+    if (j + 1 < ntk) tile_step(k_lds1, v_lds1, k_lds0, v_lds0, j + 1);
   }
 
 #pragma unroll
@@ -426,6 +488,8 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
                             hipStream_t st) {
   if (d == 128 && bm == 64 && bn == 128)
     return launch_dkdv_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, n, scale, causal, st);
+  if (d == 128 && bm == 128 && bn == 128)
+    return launch_dkdv_inst<128, 32, 4, 128>(q, k, v, dO, lse, delta, dk, dv, bh, n, scale, causal, st);
   if (d == 64 && bm == 64 && bn == 128)
     return launch_dkdv_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, n, scale, causal, st);
   return hipErrorInvalidValue;

@@ -71,74 +71,115 @@ __device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tiles in LDS: [rows][D] elements stored in 16-byte chunks, chunk c of
-// row r placed at chunk position c ^ sigma(r), with
-//   sigma(r) = 2 * (r mod H) + ((r / H) mod 2),  H = D / 16.
-// sigma is a permutation of the D/8 chunk positions over any D/8 consecutive
-// rows (a 16-lane natural read of one chunk from 16 rows hits distinct
-// positions when D = 128), and sigma / 2 is distinct over H consecutive rows
-// (the 8 rows x 2 chunks of a transposed read spread over all positions).
+// bf16 tiles in LDS: [rows][D] elements in 16-byte chunks (D/8 per row, no
+// padding).  Chunk c of row r is stored at chunk position c ^ sigma(r).
+//
+// gfx950 LDS, as measured with SQ_LDS_BANK_CONFLICT on probe kernels: 64
+// banks of 4 bytes (256 bytes per clock).  ds_read_b128 serves 16 lanes per
+// clock, the lanes that agree on lane bit 5 and on the parity of lane bits
+// 2..4; ds_read_b64_tr_b16 serves 32 consecutive lanes per clock.  The two
+// reads every operand tile sees are
+// * natural: lane (g = lane / 16, l16 = lane % 16) reads chunk 4 ds + g of
+//   row R0 + l16 (R0 a multiple of 16);
+// * transposed: lane (g, l16) reads half of chunk 2 db + (l16 / 2) % 2 of row
+//   R0 + 4 g + l16 / 4.
+// sigma below makes both conflict-free (checked exhaustively against that
+// model for every ds, db and R0): for D = 128, sigma(r) = (r mod 16) xor
+// (12 (r mod 2)); for D = 64 (two rows per bank sweep), sigma(r) = r and 6.
+// The readers precompute one offset per ds / db step for each lane, so the
+// unrolled loops read with immediate offsets only.
 // ---------------------------------------------------------------------------
 template <int D>
-struct SwzTile {
-  static constexpr int NCH = D / 8;
-  static constexpr int H = D / 16;
-  __device__ __forceinline__ static int chunk_pos(int r, int c) {
-    return c ^ (2 * (r % H) + ((r / H) & 1));
+__device__ __forceinline__ int swz_sigma(int r) {
+  static_assert(D == 64 || D == 128, "bf16 tiles are 64 or 128 wide");
+  if constexpr (D == 128) return (r & 15) ^ (12 * (r & 1));
+  else return r & 6;
+}
+
+// Natural read of the operand "row R0 + l16, 8 elements at column 32 ds + 8 g"
+// (R0 a multiple of 16).
+template <int D>
+struct NatReader {
+  static constexpr int NDS = D / 32;
+  int off[NDS];   // element offsets for R0 = 0
+  __device__ __forceinline__ NatReader(int l16, int g) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) off[ds] = l16 * D + 8 * ((4 * ds + g) ^ swz_sigma<D>(l16));
   }
-  // element offset of (row, col)
-  __device__ __forceinline__ static int off(int r, int col) {
-    return r * D + (chunk_pos(r, col >> 3) << 3) + (col & 7);
+  // r0 and ds must be compile-time constants after unrolling.
+  __device__ __forceinline__ bf16x8 read(const __bf16* tile, int r0, int ds) const {
+    return *reinterpret_cast<const bf16x8*>(tile + off[ds] + r0 * D);
   }
 };
 
-// 8 consecutive bf16 (one 16-byte chunk) at logical (row, 8 * chunk).
+// Transposed read: lane (g, l16) receives the 4 elements of column
+// 16 db + l16 in rows R0 + 4 g .. R0 + 4 g + 3 (R0 a multiple of 16).
 template <int D>
-__device__ __forceinline__ bf16x8 lds_read_chunk(const __bf16* tile, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(tile + SwzTile<D>::off(row, chunk * 8));
-}
-
-// Transposed read of a 4 x 16 block of a row-major tile: every lane of a
-// 16-lane group passes the same `row` and `col0`; lane `lane16` of the group
-// receives the 4 elements of column col0 + lane16 in rows row .. row+3.
-template <int D>
-__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* tile, int row, int col0, int lane16) {
-  const __bf16* p = tile + SwzTile<D>::off(row + (lane16 >> 2), col0 + 4 * (lane16 & 3));
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (__attribute__((address_space(3))) bf16x4*)(p));
-}
-
-// Copy `rows` x D bf16 rows (global row-major, row stride D) into a swizzled
-// LDS tile with the whole workgroup; rows at or past `valid` are zero-filled.
-// Staging through registers: `load` fills regs, `store` writes them.
-template <int D, int ROWS, int NTHREADS>
-struct TileCopy {
-  static constexpr int NCH = D / 8;
-  static constexpr int CHUNKS = ROWS * NCH;
-  static constexpr int PER_THREAD = (CHUNKS + NTHREADS - 1) / NTHREADS;
-  static_assert(CHUNKS % NTHREADS == 0, "tile chunks must divide evenly over threads");
-  u32x4 reg[PER_THREAD];
-
-  __device__ __forceinline__ void load(const __bf16* g, int valid, int tid) {
+struct TrReader {
+  static constexpr int NDB = D / 16;
+  int off[NDB];
+  __device__ __forceinline__ TrReader(int l16, int g) {
+    const int row = 4 * g + (l16 >> 2);
 #pragma unroll
-    for (int it = 0; it < PER_THREAD; ++it) {
-      const int u = tid + it * NTHREADS;
-      const int r = u / NCH, c = u % NCH;
-      if (r < valid) {
-        reg[it] = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + c * 8);
-      } else {
-        reg[it] = u32x4{0u, 0u, 0u, 0u};
+    for (int db = 0; db < NDB; ++db)
+      off[db] = row * D + 8 * ((2 * db + ((l16 >> 1) & 1)) ^ swz_sigma<D>(row)) + 4 * (l16 & 1);
+  }
+  __device__ __forceinline__ bf16x4 read(const __bf16* tile, int r0, int db) const {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(tile + off[db] + r0 * D));
+  }
+};
+
+// Asynchronous copy of a ROWS x D bf16 tile (global, row stride D) into a
+// swizzled LDS tile with global_load_lds_dwordx4: lane i of a wave writes the
+// 16 bytes at LDS chunk slot (base + i), so each lane fetches the global chunk
+// that belongs at that slot.  The per-lane source offsets are fixed for a
+// given tile shape, so they are computed once; a tile with fewer than ROWS
+// valid rows re-reads its last valid row in place of the missing ones (finite
+// values that the caller masks).  Every wave of the workgroup issues
+// ROWS * D / 8 / 64 / NW instructions.
+template <int D, int ROWS, int NW>
+struct AsyncTileCopy {
+  static constexpr int NCH = D / 8;
+  static constexpr int PER_WAVE = ROWS * NCH / 64 / NW;
+  static_assert((ROWS * NCH / 64) % NW == 0, "tile must split evenly over the waves");
+  int src_off[PER_WAVE];   // element offset of this lane's chunk in the global tile
+  int row[PER_WAVE];       // its row
+  int lds_off[PER_WAVE];   // element offset of this wave's 64-chunk slot block (uniform)
+
+  __device__ __forceinline__ AsyncTileCopy(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int slot0 = (i * NW + wave) * 64;
+      const int p = slot0 + lane;
+      const int r = p / NCH;
+      const int c = (p % NCH) ^ swz_sigma<D>(r);
+      row[i] = r;
+      src_off[i] = r * D + c * 8;
+      lds_off[i] = slot0 * 8;
+    }
+  }
+  // Copy rows [0, ROWS) of the tile starting at g; `valid` >= 1 rows exist.
+  __device__ __forceinline__ void issue(__bf16* tile, const __bf16* g, int valid) const {
+    if (valid >= ROWS) {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) issue_one(tile + lds_off[i], g + src_off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int off = row[i] < valid ? src_off[i] : src_off[i] - (row[i] - valid + 1) * D;
+        issue_one(tile + lds_off[i], g + off);
       }
     }
   }
-  __device__ __forceinline__ void store(__bf16* tile, int tid) const {
-#pragma unroll
-    for (int it = 0; it < PER_THREAD; ++it) {
-      const int u = tid + it * NTHREADS;
-      const int r = u / NCH, c = u % NCH;
-      *reinterpret_cast<u32x4*>(tile + r * D + (SwzTile<D>::chunk_pos(r, c) << 3)) = reg[it];
-    }
+  __device__ __forceinline__ static void issue_one(__bf16* lds, const __bf16* src) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
   }
 };
+
+// Wait until this wave's asynchronous LDS copies have landed (the barrier
+// that follows makes them visible to the workgroup).
+__device__ __forceinline__ void async_copy_wait() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace fa
