@@ -23,6 +23,8 @@
 // * Causal mode visits only the tiles that hold a visible (query, key) pair
 //   and masks only tiles crossing the diagonal.  Workgroups are ordered with
 //   the heaviest tiles first.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -43,7 +45,8 @@ __device__ __forceinline__ void rows_load_async(float* lds, const float* src, in
   }
 }
 
-template <int D, int KW, int NW, int BR, bool CAUSAL>
+// RAGGED: n may not be a multiple of BR (the last query tile needs the mask).
+template <int D, int KW, int NW, int BR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(NW * 64, 1)
 void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -119,48 +122,26 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   async_copy_wait();
   __syncthreads();
 
-  // Stages of one 32-query step t of a query tile (software-pipelined below:
-  // the S/dP products of step t+1 are issued while the VALU turns step t into
-  // P and dS, so the matrix cores are not idle during the softmax work).
+  // One 32-query step t of a query tile has three stages:
+  //   G1(t): S = Q K^T and dP = dO V^T          (2 D/32 MFMA groups of 2 NKB)
+  //   EW(t): P = exp(S - L), dS = P (dP - D)    (16 elementwise items per lane)
+  //   G2(t): dV^T += dO^T P, dK^T += Q^T dS      (D/16 MFMA groups of 2 NKB)
+  // They run as a software pipeline, G2(t-1) | EW(t) | G1(t+1), with the
+  // elementwise items of EW(t) spread over the MFMA groups of G2(t-1) and
+  // G1(t+1): every fenced group holds a few MFMAs, the LDS reads for a later
+  // group and one or two elementwise items, so the VALU work and the LDS
+  // latency both hide behind the matrix cores within the one wave per SIMD.
   using Acc = f32x4[2][NKB];
-  auto stage_sdp = [&](const __bf16* qt, const __bf16* ot, int t, Acc& s, Acc& dp) __attribute__((always_inline)) {
-    // S = Q K^T and dP = dO V^T: lane holds query 32t + 16h + 4g + i, key 16kb + l16.
-    // Operands are read PF steps ahead of their MFMAs (see the dQ kernel).
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    constexpr int PF = 3, U = NDS * 2;             // steps: (ds, h)
-    bf16x8 qa[PF], oa[PF];
-#pragma unroll
-    for (int u = 0; u < PF && u < U; ++u) {
-      qa[u] = nat.read(qt, 32 * t + 16 * (u & 1), u >> 1);
-      oa[u] = nat.read(ot, 32 * t + 16 * (u & 1), u >> 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ds = u >> 1, h = u & 1;
-      const bf16x8 aq = qa[u % PF], ao = oa[u % PF];
-      if (u + PF < U) {
-        qa[u % PF] = nat.read(qt, 32 * t + 16 * ((u + PF) & 1), (u + PF) >> 1);
-        oa[u % PF] = nat.read(ot, 32 * t + 16 * ((u + PF) & 1), (u + PF) >> 1);
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[h][kb] = mfma_bf16(aq, kf[kb][ds], s[h][kb]);
-        dp[h][kb] = mfma_bf16(ao, vf[kb][ds], dp[h][kb]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  constexpr int NG1 = 2 * NDS;                   // MFMA groups of G1: (ds, h)
+  constexpr int NG2 = NDB;                       // MFMA groups of G2: db
+  constexpr int NE = 2 * 4 * NKB;                // elementwise items per lane per step
+  constexpr int PF = 2;                          // operand prefetch distance (groups)
+
+  struct EwState {
+    float l2[2][4], dd[2][4];
+    f32x4 pv[2][NKB], dsv[2][NKB];
   };
-  // P = exp(S - L) (Eq 14) and dS = P (dP - D) (Eq 17), packed to bf16 operands
-  auto stage_pds = [&](const float* lt, const float* dt, int i0, int t, bool need_mask,
-                       const Acc& s, const Acc& dp, bf16x8 (&pb)[NKB], bf16x8 (&sb)[NKB]) __attribute__((always_inline)) {
-    f32x4 pv[2][NKB], dv4[2][NKB];
+  auto ew_begin = [&](const float* lt, const float* dt, int t, EwState& e) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int rl = 32 * t + 16 * h + 4 * g;     // first of this lane's 4 rows
@@ -168,67 +149,152 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rl);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float l2 = l4[i] * kLog2e;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          float p = exp2_fast(__builtin_fmaf(s[h][kb][i], scale_log2, -l2));
-          if (need_mask) {
-            const int q = i0 + rl + i;
-            if ((CAUSAL && k0w + 16 * kb + l16 > q) || q >= n) p = 0.f;
-          }
-          pv[h][kb][i] = p;
-          dv4[h][kb][i] = p * (dp[h][kb][i] - d4[i]);
-        }
+        e.l2[h][i] = l4[i] * kLog2e;
+        e.dd[h][i] = d4[i];
       }
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      pb[kb] = pack_bf16(pv[0][kb], pv[1][kb]);
-      sb[kb] = pack_bf16(dv4[0][kb], dv4[1][kb]);
     }
   };
-  // dV^T += dO^T P (Eq 15) and dK^T += Q^T dS (Eq 19, scale applied at the end)
-  auto stage_dvdk = [&](const __bf16* qt, const __bf16* ot, int t, const bf16x8 (&pb)[NKB],
-                        const bf16x8 (&sb)[NKB]) __attribute__((always_inline)) {
-    constexpr int PF = 3, U = NDB;                 // steps: db
-    bf16x8 oa[PF], qa[PF];
+  // item x = (h, i, kb) of step t
+  auto ew_item = [&](int x, int i0, int t, bool need_mask, const Acc& s, const Acc& dp, EwState& e) __attribute__((always_inline)) {
+    const int kb = x % NKB, i = (x / NKB) % 4, h = x / (4 * NKB);
+    const float p = exp2_fast(__builtin_fmaf(s[h][kb][i], scale_log2, -e.l2[h][i]));
+    e.pv[h][kb][i] = p;
+    e.dsv[h][kb][i] = p * (dp[h][kb][i] - e.dd[h][i]);
+  };
+  // Masked entries (key after query, or query past n) get P = dS = 0.  Only
+  // tiles crossing the diagonal or the end of the sequence run this, behind
+  // a uniform branch, so the other tiles carry no mask arithmetic.
+  auto ew_mask = [&](int i0, int t, EwState& e) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < PF && u < U; ++u) {
-      oa[u] = cat(tr.read(ot, 32 * t, u), tr.read(ot, 32 * t + 16, u));
-      qa[u] = cat(tr.read(qt, 32 * t, u), tr.read(qt, 32 * t + 16, u));
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bf16x8 ao = oa[u % PF], aq = qa[u % PF];
-      if (u + PF < U) {
-        oa[u % PF] = cat(tr.read(ot, 32 * t, u + PF), tr.read(ot, 32 * t + 16, u + PF));
-        qa[u % PF] = cat(tr.read(qt, 32 * t, u + PF), tr.read(qt, 32 * t + 16, u + PF));
+      for (int i = 0; i < 4; ++i) {
+        const int q = i0 + 32 * t + 16 * h + 4 * g + i;
+        const int lim = (q < n) ? (CAUSAL ? q - k0w - l16 : 0x7fffffff) : -1;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          if (16 * kb > lim) {
+            e.pv[h][kb][i] = 0.f;
+            e.dsv[h][kb][i] = 0.f;
+          }
       }
+  };
+  auto ew_end = [&](const EwState& e, bf16x8 (&pb)[NKB], bf16x8 (&sb)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        dv[u][kb] = mfma_bf16(ao, pb[kb], dv[u][kb]);
-        dk[u][kb] = mfma_bf16(aq, sb[kb], dk[u][kb]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int kb = 0; kb < NKB; ++kb) {
+      pb[kb] = pack_bf16(e.pv[0][kb], e.pv[1][kb]);
+      sb[kb] = pack_bf16(e.dsv[0][kb], e.dsv[1][kb]);
     }
   };
 
-  // The steps of a tile run as a three-stage software pipeline: dV/dK of
-  // step t-1, then P/dS of step t, then S/dP of step t+1 (independent work
-  // back to back, so MFMAs still in flight overlap the VALU stage).
-  auto pipelined = [&](const __bf16* qt, const __bf16* ot, const float* lt, const float* dt,
-                       int i0, bool need_mask) __attribute__((always_inline)) {
+  // Operand reads for group u of G1 (natural Q, dO rows) and of G2 (transposed).
+  auto g1_read = [&](const __bf16* qt, const __bf16* ot, int t, int u, bf16x8& aq, bf16x8& ao) __attribute__((always_inline)) {
+    aq = nat.read(qt, 32 * t + 16 * (u & 1), u >> 1);
+    ao = nat.read(ot, 32 * t + 16 * (u & 1), u >> 1);
+  };
+  auto g2_read = [&](const __bf16* qt, const __bf16* ot, int t, int u, bf16x8& aq, bf16x8& ao) __attribute__((always_inline)) {
+    ao = cat(tr.read(ot, 32 * t, u), tr.read(ot, 32 * t + 16, u));
+    aq = cat(tr.read(qt, 32 * t, u), tr.read(qt, 32 * t + 16, u));
+  };
+  auto g1_mfma = [&](int u, const bf16x8& aq, const bf16x8& ao, Acc& s, Acc& dp) __attribute__((always_inline)) {
+    const int ds = u >> 1, h = u & 1;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[h][kb] = mfma_bf16(aq, kf[kb][ds], s[h][kb]);
+      dp[h][kb] = mfma_bf16(ao, vf[kb][ds], dp[h][kb]);
+    }
+  };
+  auto g2_mfma = [&](int u, const bf16x8& aq, const bf16x8& ao, const bf16x8 (&pb)[NKB], const bf16x8 (&sb)[NKB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      dv[u][kb] = mfma_bf16(ao, pb[kb], dv[u][kb]);
+      dk[u][kb] = mfma_bf16(aq, sb[kb], dk[u][kb]);
+    }
+  };
+  auto zero_acc = [&](Acc& s, Acc& dp) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  };
+
+  // One query tile: the pipeline over its NQS steps.  The operand stream of a
+  // pipeline region is the concatenation [G2(t-1) groups] [G1(t+1) groups];
+  // reads run PF groups ahead along that stream.
+  auto run_tile = [&](const __bf16* qt, const __bf16* ot, const float* lt, const float* dt, int i0,
+                      auto masked) __attribute__((always_inline)) {
+    constexpr bool need_mask = decltype(masked)::value;
     Acc sa[2], pa[2];
     bf16x8 pbuf[2][NKB], sbuf[2][NKB];
-    stage_sdp(qt, ot, 0, sa[0], pa[0]);
+    // prologue: G1(0) alone
+    {
+      zero_acc(sa[0], pa[0]);
+      bf16x8 rq[PF], ro[PF];
+#pragma unroll
+      for (int u = 0; u < PF; ++u) g1_read(qt, ot, 0, u, rq[u], ro[u]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < NG1; ++u) {
+        const bf16x8 aq = rq[u % PF], ao = ro[u % PF];
+        if (u + PF < NG1) g1_read(qt, ot, 0, u + PF, rq[u % PF], ro[u % PF]);
+        g1_mfma(u, aq, ao, sa[0], pa[0]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < NQS; ++t) {
-      if (t >= 1) stage_dvdk(qt, ot, t - 1, pbuf[(t - 1) & 1], sbuf[(t - 1) & 1]);
-      stage_pds(lt, dt, i0, t, need_mask, sa[t & 1], pa[t & 1], pbuf[t & 1], sbuf[t & 1]);
-      if (t + 1 < NQS) stage_sdp(qt, ot, t + 1, sa[(t + 1) & 1], pa[(t + 1) & 1]);
+      const bool has_g2 = t >= 1, has_g1 = t + 1 < NQS;
+      const int ngroups = (has_g2 ? NG2 : 0) + (has_g1 ? NG1 : 0);
+      EwState e;
+      ew_begin(lt, dt, t, e);
+      if (has_g1) zero_acc(sa[(t + 1) & 1], pa[(t + 1) & 1]);
+      // read group v of the region's operand stream
+      auto read_v = [&](int v, bf16x8& aq, bf16x8& ao) __attribute__((always_inline)) {
+        if (has_g2 && v < NG2) g2_read(qt, ot, t - 1, v, aq, ao);
+        else g1_read(qt, ot, t + 1, v - (has_g2 ? NG2 : 0), aq, ao);
+      };
+      bf16x8 rq[PF], ro[PF];
+#pragma unroll
+      for (int v = 0; v < PF; ++v) read_v(v, rq[v], ro[v]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int v = 0; v < NG1 + NG2; ++v) {
+        if (v < ngroups) {
+          const bf16x8 aq = rq[v % PF], ao = ro[v % PF];
+          if (v + PF < ngroups) read_v(v + PF, rq[v % PF], ro[v % PF]);
+          if (has_g2 && v < NG2) g2_mfma(v, aq, ao, pbuf[(t - 1) & 1], sbuf[(t - 1) & 1]);
+          else g1_mfma(v - (has_g2 ? NG2 : 0), aq, ao, sa[(t + 1) & 1], pa[(t + 1) & 1]);
+          // spread the NE elementwise items of step t over the region's groups
+#pragma unroll
+          for (int x = (v * NE) / ngroups; x < ((v + 1) * NE) / ngroups; ++x)
+            ew_item(x, i0, t, need_mask, sa[t & 1], pa[t & 1], e);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (ngroups == 0) {
+#pragma unroll
+        for (int x = 0; x < NE; ++x) ew_item(x, i0, t, need_mask, sa[t & 1], pa[t & 1], e);
+      }
+      if constexpr (need_mask) ew_mask(i0, t, e);
+      ew_end(e, pbuf[t & 1], sbuf[t & 1]);
     }
-    stage_dvdk(qt, ot, NQS - 1, pbuf[(NQS - 1) & 1], sbuf[(NQS - 1) & 1]);
+    // epilogue: G2 of the last step alone
+    {
+      bf16x8 rq[PF], ro[PF];
+#pragma unroll
+      for (int u = 0; u < PF; ++u) g2_read(qt, ot, NQS - 1, u, rq[u], ro[u]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < NG2; ++u) {
+        const bf16x8 aq = rq[u % PF], ao = ro[u % PF];
+        if (u + PF < NG2) g2_read(qt, ot, NQS - 1, u + PF, rq[u % PF], ro[u % PF]);
+        g2_mfma(u, aq, ao, pbuf[(NQS - 1) & 1], sbuf[(NQS - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
   auto tile_step = [&](const __bf16* qt, const __bf16* ot, const float* lt, const float* dt,
@@ -237,13 +303,19 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     if (it + 1 < ntq) issue_tile(qn, on, ln, dn, i0 + BR);
     const bool active = !CAUSAL || (i0 + BR - 1 >= k0w);
     if (active) {
-      // only tiles crossing the diagonal or the end of the sequence are masked
-      pipelined(qt, ot, lt, dt, i0, (CAUSAL && i0 < k0w + KW - 1) || (i0 + BR > n));
+      // only tiles crossing the diagonal or the end of the sequence are masked;
+      // they run a separate copy so that the others carry no mask arithmetic
+      if ((CAUSAL || RAGGED) && ((CAUSAL && i0 < k0w + KW - 1) || (i0 + BR > n))) {
+        run_tile(qt, ot, lt, dt, i0, std::true_type{});
+      } else {
+        run_tile(qt, ot, lt, dt, i0, std::false_type{});
+      }
     }
     async_copy_wait();
     __syncthreads();
   };
 
+#pragma unroll 1
   for (int it = it0; it < ntq; it += 2) {
     tile_step(q_lds0, o_lds0, l_lds0, d_lds0, q_lds1, o_lds1, l_lds1, d_lds1, it);
     if (it + 1 < ntq) tile_step(q_lds1, o_lds1, l_lds1, d_lds1, q_lds0, o_lds0, l_lds0, d_lds0, it + 1);
@@ -379,17 +451,27 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       }
       const bool need_mask = (CAUSAL && j0 + BC - 1 > q0w) || (j0 + BC > n);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int last = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
-        const int lim = last - j0 - 4 * g;     // key j0 + 16kb + 4g + i visible iff 16kb + i <= lim
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float p = exp2_fast(__builtin_fmaf(s[kb][qb][i], scale_log2, -l2q[qb]));
-            if (need_mask && 16 * kb + i > lim) p = 0.f;
+            const float p = exp2_fast(__builtin_fmaf(s[kb][qb][i], scale_log2, -l2q[qb]));
             dp[kb][qb][i] = p * (dp[kb][qb][i] - dq_d[qb]);
           }
+      // masked entries get dS = 0; only tiles crossing the diagonal or the end
+      // of the sequence run this, behind a uniform branch
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int last = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
+          const int lim = last - j0 - 4 * g;   // key j0 + 16kb + 4g + i visible iff 16kb + i <= lim
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * kb + i > lim) dp[kb][qb][i] = 0.f;
+        }
       }
       // dQ^T += K^T dS^T (Eq 18, scale applied at the end)
       bf16x8 sb[NKS][NQB];
@@ -421,6 +503,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __syncthreads();
   };
 
+#pragma unroll 1
   for (int j = 0; j < ntk; j += 2) {
     tile_step(k_lds0, v_lds0, k_lds1, v_lds1, j);
     if (j + 1 < ntk) tile_step(k_lds1, v_lds1, k_lds0, v_lds0, j + 1);
@@ -449,15 +532,13 @@ static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, 
   const int ntk = (n + BC - 1) / BC;
   const dim3 grid((unsigned)(ntk * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
-  if (causal) {
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KW, NW, BR, true>), grid, block, 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dk, (__bf16*)dv, bh, n, scale, sl2);
-  } else {
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, KW, NW, BR, false>), grid, block, 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dk, (__bf16*)dv, bh, n, scale, sl2);
-  }
+  // the non-causal kernel keeps its masked copy even when n is a multiple of
+  // BR: the uniform branch around it splits the tile into scheduling regions
+  // small enough to stay within the register file
+  auto kern = causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true>
+                     : dkdv_bf16_kernel<D, KW, NW, BR, false, true>;
+  hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                     (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, bh, n, scale, sl2);
   return hipGetLastError();
 }
 

@@ -30,6 +30,8 @@
 // * Workgroup ids are mapped heaviest query tile first (causal work grows
 //   with the tile index), and head = id mod bh keeps every tile of a head on
 //   one XCD (ids are dealt to the 8 XCDs round robin) for L2 reuse of K/V.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -37,7 +39,8 @@ namespace fa {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int QW, int NW, int BC, bool CAUSAL>
+// RAGGED: n may not be a multiple of BC (the last key tile needs the mask).
+template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(NW * 64, (QW >= 64 ? 1 : 2))
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -102,16 +105,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   async_copy_wait();
   __syncthreads();
 
-  // One key tile: prefetch tile j+1 into (kn, vn), compute tile j from (kt, vt).
-  auto tile_step = [&](const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn, int j) __attribute__((always_inline)) {
-    const int j0 = j * BC;
-    if (j + 1 < ntk) {
-      copier.issue(kn, Kh + (size_t)(j0 + BC) * D, n - j0 - BC);
-      copier.issue(vn, Vh + (size_t)(j0 + BC) * D, n - j0 - BC);
-    }
-    // a wave whose rows all precede the tile has nothing to do in it
-    const bool active = !CAUSAL || (j0 <= q0w + QW - 1);
-    if (active) {
+  // The work of one key tile; `masked` (a compile-time flag) selects the copy
+  // with the in-tile mask, used only by tiles crossing the diagonal or the end
+  // of the sequence, so that the other tiles carry no mask arithmetic.
+  auto tile_compute = [&](const __bf16* kt, const __bf16* vt, int j0, auto masked) __attribute__((always_inline)) {
+    {
       // S^T[key][query] = K Q^T: lane holds key 16kb + 4g + i, query 16qb + l16
       f32x4 s[NKB][NQB];
 #pragma unroll
@@ -137,9 +135,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // in-tile mask, only on tiles crossing the diagonal or the end of the
-      // sequence: key j0 + 16kb + 4g + i is visible iff 16kb + i <= lim
-      if ((CAUSAL && j0 + BC - 1 > q0w) || (j0 + BC > n)) {
+      // in-tile mask: key j0 + 16kb + 4g + i is visible iff 16kb + i <= lim
+      if constexpr (decltype(masked)::value) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const int last = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
@@ -164,7 +161,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         mx[qb] = wave_max_xor16_32(t) * scale_log2;
         grow |= !(mx[qb] <= m[qb] + kRescaleSlack);   // also true while m = -inf
       }
-      if (__any(grow)) {
+      // uniform branch (the vote is read into a scalar register)
+      if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const float m_new = fmaxf(m[qb], mx[qb]);
@@ -214,10 +212,28 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
       }
     }
+  };
+
+  // One key tile: prefetch tile j+1 into (kn, vn), compute tile j from (kt, vt).
+  auto tile_step = [&](const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn, int j) __attribute__((always_inline)) {
+    const int j0 = j * BC;
+    if (j + 1 < ntk) {
+      copier.issue(kn, Kh + (size_t)(j0 + BC) * D, n - j0 - BC);
+      copier.issue(vn, Vh + (size_t)(j0 + BC) * D, n - j0 - BC);
+    }
+    // a wave whose rows all precede the tile has nothing to do in it
+    if (!CAUSAL || (j0 <= q0w + QW - 1)) {
+      if ((CAUSAL || RAGGED) && ((CAUSAL && j0 + BC - 1 > q0w) || (j0 + BC > n))) {
+        tile_compute(kt, vt, j0, std::true_type{});
+      } else {
+        tile_compute(kt, vt, j0, std::false_type{});
+      }
+    }
     async_copy_wait();
     __syncthreads();
   };
 
+#pragma unroll 1
   for (int j = 0; j < ntk; j += 2) {
     tile_step(k_lds0, v_lds0, k_lds1, v_lds1, j);
     if (j + 1 < ntk) tile_step(k_lds1, v_lds1, k_lds0, v_lds0, j + 1);
@@ -250,13 +266,11 @@ static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, v
   const int ntq = (n + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
-  if (causal) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QW, NW, BC, true>), grid, block, 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, bh, n, sl2);
-  } else {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QW, NW, BC, false>), grid, block, 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, bh, n, sl2);
-  }
+  auto kern = causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true>
+            : (n % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true>
+                       : fwd_bf16_kernel<D, QW, NW, BC, false, false>;
+  hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                     (__bf16*)o, lse, bh, n, sl2);
   return hipGetLastError();
 }
 
@@ -265,10 +279,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int bh, int n, int d, float scale, int causal, int bm, int bn,
                            hipStream_t st) {
   if (d == 128 && bm == 128 && bn == 64) return launch_fwd_inst<128, 32, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
-  if (d == 128 && bm == 256 && bn == 64) return launch_fwd_inst<128, 64, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
+  if (d == 128 && bm == 256 && bn == 64) return launch_fwd_inst<128, 32, 8, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
   if (d == 128 && bm == 128 && bn == 128) return launch_fwd_inst<128, 32, 4, 128>(q, k, v, o, lse, bh, n, scale, causal, st);
   if (d == 64 && bm == 128 && bn == 64) return launch_fwd_inst<64, 32, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
-  if (d == 64 && bm == 256 && bn == 64) return launch_fwd_inst<64, 64, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
+  if (d == 64 && bm == 256 && bn == 64) return launch_fwd_inst<64, 32, 8, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
   return hipErrorInvalidValue;
 }
 
