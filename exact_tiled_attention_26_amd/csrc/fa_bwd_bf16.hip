@@ -80,7 +80,8 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   const int ntq = (n + BR - 1) / BR;
   const int it0 = CAUSAL ? (k0 / BR) : 0;   // earlier query rows see none of these keys
-  const AsyncTileCopy<D, BR, NW> copier(wave, lane);
+  // compiler-visible copies: measured faster than the hidden form here
+  const AsyncTileCopy<D, BR, NW, false> copier(wave, lane);
   auto issue_tile = [&](__bf16* qd, __bf16* od, float* ld, float* dd, int i0) __attribute__((always_inline)) {
     copier.issue(qd, Qh + (size_t)i0 * D, n - i0);
     copier.issue(od, dOh + (size_t)i0 * D, n - i0);
@@ -371,7 +372,8 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   const int kend = CAUSAL ? min(n, q0 + BR) : n;
   const int ntk = (kend + BC - 1) / BC;
-  const AsyncTileCopy<D, BC, NW> copier(wave, lane);
+  // compiler-visible copies: measured faster than the hidden form here
+  const AsyncTileCopy<D, BC, NW, false> copier(wave, lane);
   copier.issue(k_lds0, Kh, min(BC, n));
   copier.issue(v_lds0, Vh, min(BC, n));
 

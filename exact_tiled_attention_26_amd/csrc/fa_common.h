@@ -51,10 +51,33 @@ __device__ __forceinline__ float wave_max_xor16_32(float x) {
   return x;
 }
 
+// Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap instructions: permlane32_swap(x, x) returns x of the
+// lower half in both halves of its first result and x of the upper half in
+// both halves of its second, permlane16_swap likewise for adjacent rows.  No
+// LDS traffic, so the LDS counter is left to the operand reads.
+__device__ __forceinline__ float wave_max_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float wave_sum_xor16_32(float x) {
   x += __shfl_xor(x, 16);
   x += __shfl_xor(x, 32);
   return x;
+}
+
+// A zero that the compiler must treat as a per-lane value.  Added to the
+// bounds that select between copies of a software-pipelined loop body, it
+// makes those branches divergent in the compiler's eyes (they are uniform in
+// fact): with provably uniform conditions the compiler moves work between
+// the copies and runs out of registers.
+__device__ __forceinline__ int divergent_zero() {
+  int z;
+  __asm__ volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
 }
 
 // Pack two 4-float accumulator fragments into one bf16x8 operand
@@ -130,6 +153,29 @@ struct TrReader {
   }
 };
 
+// HBM -> LDS copies without staging registers: global_load_lds_dwordx4
+// writes the 16 bytes that lane i loads from gbase + byte_off to LDS address
+// M0 + 16i; M0 holds the wave's LDS destination and must be
+// written one wait state before the load.
+//
+// Two ways to issue them.  The compiler builtin lets the compiler see the
+// copy; its wait-count analysis then treats the pending copy as an LDS
+// access of unknown completion order and waits for every outstanding LDS
+// read (lgkmcnt(0)) at each operand use.  The inline-assembly form below
+// hides the copy: the compiler's own vmcnt waits only become stricter (the
+// counter retires in issue order) and its lgkmcnt waits stay exact, and
+// completion is the caller's job: async_copy_wait() and a barrier before any
+// wave reads the data.  No other code here uses M0; the LDS address is the
+// same in every lane and is read into a scalar register.  Which form is
+// faster depends on the kernel's schedule (measured per kernel).
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void lds_dma16(const void* gbase, unsigned byte_off, const void* lds) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(byte_off), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_address(lds))) : "memory");
+}
+
 // Asynchronous copy of a ROWS x D bf16 tile (global, row stride D) into a
 // swizzled LDS tile with global_load_lds_dwordx4: lane i of a wave writes the
 // 16 bytes at LDS chunk slot (base + i), so each lane fetches the global chunk
@@ -138,13 +184,13 @@ struct TrReader {
 // valid rows re-reads its last valid row in place of the missing ones (finite
 // values that the caller masks).  Every wave of the workgroup issues
 // ROWS * D / 8 / 64 / NW instructions.
-template <int D, int ROWS, int NW>
+// HIDDEN selects the inline-assembly copy (see lds_dma16) over the builtin.
+template <int D, int ROWS, int NW, bool HIDDEN = true>
 struct AsyncTileCopy {
   static constexpr int NCH = D / 8;
   static constexpr int PER_WAVE = ROWS * NCH / 64 / NW;
   static_assert((ROWS * NCH / 64) % NW == 0, "tile must split evenly over the waves");
   int src_off[PER_WAVE];   // element offset of this lane's chunk in the global tile
-  int row[PER_WAVE];       // its row
   int lds_off[PER_WAVE];   // element offset of this wave's 64-chunk slot block (uniform)
 
   __device__ __forceinline__ AsyncTileCopy(int wave, int lane) {
@@ -154,7 +200,6 @@ struct AsyncTileCopy {
       const int p = slot0 + lane;
       const int r = p / NCH;
       const int c = (p % NCH) ^ swz_sigma<D>(r);
-      row[i] = r;
       src_off[i] = r * D + c * 8;
       lds_off[i] = slot0 * 8;
     }
@@ -163,23 +208,34 @@ struct AsyncTileCopy {
   __device__ __forceinline__ void issue(__bf16* tile, const __bf16* g, int valid) const {
     if (valid >= ROWS) {
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) issue_one(tile + lds_off[i], g + src_off[i]);
+      for (int i = 0; i < PER_WAVE; ++i) issue_one(tile + lds_off[i], g, src_off[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
-        const int off = row[i] < valid ? src_off[i] : src_off[i] - (row[i] - valid + 1) * D;
-        issue_one(tile + lds_off[i], g + off);
+        const int row = src_off[i] / D;   // D is a power of two
+        const int off = row < valid ? src_off[i] : src_off[i] - (row - valid + 1) * D;
+        issue_one(tile + lds_off[i], g, off);
       }
     }
   }
-  __device__ __forceinline__ static void issue_one(__bf16* lds, const __bf16* src) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  __device__ __forceinline__ static void issue_one(__bf16* lds, const __bf16* g, int off) {
+    if constexpr (HIDDEN) {
+      lds_dma16(g, 2u * off, lds);
+    } else {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
+                                       (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+    }
   }
 };
 
 // Wait until this wave's asynchronous LDS copies have landed (the barrier
 // that follows makes them visible to the workgroup).
 __device__ __forceinline__ void async_copy_wait() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// ... all but the N most recently issued (the counter retires in issue order).
+template <int N>
+__device__ __forceinline__ void async_copy_wait_allbut() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __asm__ volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 }  // namespace fa

@@ -38,10 +38,11 @@
 namespace fa {
 
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kFwdBuffers = 2;   // LDS buffers per operand (copy distance NBUF - 1 tiles)
 
 // RAGGED: n may not be a multiple of BC (the last key tile needs the mask).
-template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED>
-__global__ __launch_bounds__(NW * 64, (QW >= 64 ? 1 : 2))
+template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED, int NBUF>
+__global__ __launch_bounds__(NW * 64, 2)
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
                      float* __restrict__ LSE, int bh, int n, float scale_log2) {
@@ -51,11 +52,17 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   constexpr int NDS = D / 32;    // 32-wide steps over the head dim (S)
   constexpr int NDB = D / 16;    // 16-wide blocks of the head dim (O)
   constexpr int NKS = BC / 32;   // 32-key steps (PV)
+  constexpr int US = NDS * NKB;  // MFMA steps of S  (each NQB MFMAs)
+  constexpr int UP = NKS * NDB;  // MFMA steps of PV (each NQB MFMAs)
+  constexpr int NE = NKB * NQB * 4;   // probabilities per lane per tile
+  static_assert(US == UP, "the two products of a tile are interleaved step by step");
+  static_assert(NKS == 2, "probabilities are produced in two halves, one per PV half");
+  static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
 
-  // two distinct LDS buffers per operand, used in a fixed ping-pong order so
-  // that the reads of one tile provably never alias the copy into the other
-  __shared__ __bf16 k_lds0[BC * D], k_lds1[BC * D];
-  __shared__ __bf16 v_lds0[BC * D], v_lds1[BC * D];
+  // NBUF LDS buffers per operand; K runs one tile ahead of V, and every copy
+  // is issued NBUF - 1 steps before its data is used
+  __shared__ __bf16 k_lds[NBUF][BC * D];
+  __shared__ __bf16 v_lds[NBUF][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -72,9 +79,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   const int kend = CAUSAL ? min(n, q0 + BR) : n;   // keys this workgroup can see
   const int ntk = (kend + BC - 1) / BC;
+  // last key tile with a key that one of this wave's rows can see
+  // (dz: see divergent_zero)
+  const int dz = divergent_zero();
+  const int last = CAUSAL ? min(ntk - 1, (q0w + QW - 1) / BC) : ntk - 1 + dz;
   const AsyncTileCopy<D, BC, NW> copier(wave, lane);
-  copier.issue(k_lds0, Kh, min(BC, n));
-  copier.issue(v_lds0, Vh, min(BC, n));
+  copier.issue(k_lds[0], Kh, min(BC, n));
+  if (ntk > 1) copier.issue(k_lds[1], Kh + (size_t)BC * D, n - BC);
+  copier.issue(v_lds[0], Vh, min(BC, n));
 
   // Q rows of this wave as B operands: lane holds Q[q0w + 16qb + l16][32ds + 8g .. +7]
   bf16x8 qf[NQB][NDS];
@@ -96,147 +108,237 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running max (exponent base) and this lane's part of the running sum
   float m[NQB], lsum[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) { m[qb] = kNegInf; lsum[qb] = 0.f; }
 
   const NatReader<D> kread(l16, g);
   const TrReader<D> vread(l16, g);
-  async_copy_wait();
-  __syncthreads();
 
-  // The work of one key tile; `masked` (a compile-time flag) selects the copy
-  // with the in-tile mask, used only by tiles crossing the diagonal or the end
-  // of the sequence, so that the other tiles carry no mask arithmetic.
-  auto tile_compute = [&](const __bf16* kt, const __bf16* vt, int j0, auto masked) __attribute__((always_inline)) {
+  // Scores are kept transposed, S^T[key][query]: lane holds key 16kb + 4g + i
+  // of the tile and query 16qb + l16 of the wave.  Two register sets hold the
+  // scores of consecutive tiles: the products of tile t+1 are issued while
+  // the probabilities of tile t are formed (software pipelining across
+  // tiles, so matrix and vector units work at the same time).
+  f32x4 sa[NKB][NQB], sb[NKB][NQB];
+
+  // does key tile j need the in-tile mask for this wave?
+  auto tile_masked = [&](int j) __attribute__((always_inline)) {
+    return (CAUSAL && j * BC + BC - 1 > q0w) || (RAGGED && j * BC + BC > n + dz);
+  };
+  // in-tile mask: key j0 + 16kb + 4g + i is visible iff 16kb + i <= lim
+  auto mask_item = [&](f32x4 (&s)[NKB][NQB], int j0, int qb, int kb) __attribute__((always_inline)) {
+    const int lastq = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
+    const int lim = lastq - j0 - 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (16 * kb + i > lim) s[kb][qb][i] = kNegInf;
+  };
+  // scaled max (base 2) of one query block over this lane's 16 keys of the
+  // tile; the other three lanes of the query hold the rest of the row
+  auto row_max = [&](f32x4 (&s)[NKB][NQB], int qb) __attribute__((always_inline)) {
+    float t = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t = fmaxf(t, s[kb][qb][i]);
+    return t * scale_log2;
+  };
+  // raise the exponent base when some score outgrew it by the slack.  The
+  // test needs only each lane's partial max and a vote (read into a scalar
+  // register, so the branch is uniform); the full row max is formed in the
+  // rare taken branch.
+  auto update_base = [&](const float (&mx)[NQB]) __attribute__((always_inline)) {
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) grow |= !(mx[qb] <= m[qb] + kRescaleSlack);   // true while m = -inf
+    if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float m_new = fmaxf(m[qb], wave_max_rows(mx[qb]));
+        const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m[qb] - m_new);
+        m[qb] = m_new;
+        lsum[qb] *= corr;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db][qb] *= corr;
+      }
+    }
+  };
+  // S^T = K Q^T of one tile, K operands read PF steps ahead (no interleaving)
+  auto s_gemm_plain = [&](f32x4 (&s)[NKB][NQB], const __bf16* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+      const int ds = u / NKB, kb = u % NKB;
+      const bf16x8 a = kread.read(kt, 16 * kb, ds);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = mfma_bf16(a, qf[qb][ds], s[kb][qb]);
+    }
+  };
+
+  // prologue: scores of tile 0 and the first exponent base
+  async_copy_wait();
+  // copies that step 0 waits for when the distance is two steps
+  if constexpr (NBUF == 3) {
+    if (ntk > 1) copier.issue(v_lds[1], Vh + (size_t)BC * D, n - BC);
+    if (ntk > 2) copier.issue(k_lds[2], Kh + (size_t)2 * BC * D, n - 2 * BC);
+  }
+  __syncthreads();
+  s_gemm_plain(sa, k_lds[0]);
+  if (tile_masked(0)) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mask_item(sa, 0, qb, kb);
+  }
+  {
+    float mx[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) mx[qb] = row_max(sa, qb);
+    update_base(mx);
+  }
+  __syncthreads();   // every wave is done with K(0) before its buffer is refilled
+
+  // One pipelined step: probabilities and PV of tile t (scores in sc, values
+  // in vt) interleaved with the scores of tile t+1 (into sn, keys in kn).
+  //   phase A: MFMA S(t+1)       | VALU: first 3/4 of P(t)
+  //   phase B: MFMA O += V^T P^T | VALU: last 1/4 of P(t), then mask and
+  //                                row max of S(t+1)
+  auto body = [&](f32x4 (&sc)[NKB][NQB], f32x4 (&sn)[NKB][NQB], const __bf16* kn, const __bf16* vt,
+                  int t, auto has_next, auto next_masked) __attribute__((always_inline)) {
+    constexpr bool HN = decltype(has_next)::value;
+    constexpr bool NM = decltype(next_masked)::value;
+    float m_use[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) m_use[qb] = (m[qb] == kNegInf) ? 0.f : m[qb];   // never (-inf) - (-inf)
+    bf16x8 pb[NKS][NQB];
+    // probability item e: score (kb, qb, i) in the order of the PV halves
+    auto p_item = [&](int e) __attribute__((always_inline)) {
+      const int h = e / (NE / 2), r = e % (NE / 2);
+      const int qb = r / 8, kb = 2 * h + (r / 4) % 2, i = r % 4;
+      const float p = exp2_fast(__builtin_fmaf(sc[kb][qb][i], scale_log2, -m_use[qb]));
+      sc[kb][qb][i] = p;
+      lsum[qb] += p;   // fp32: the row sum sets L, which bf16 terms would not resolve
+      if (r % 8 == 7) pb[h][qb] = pack_bf16(sc[2 * h][qb], sc[2 * h + 1][qb]);
+    };
+    constexpr int EA = 3 * NE / 4;   // items done in phase A
+    // phase A
     {
-      // S^T[key][query] = K Q^T: lane holds key 16kb + 4g + i, query 16qb + l16
-      f32x4 s[NKB][NQB];
+      constexpr int PF = 3;
+      bf16x8 ka[PF];
+      // steps run key block by key block (u = kb * NDS + ds), so the
+      // accumulators of S(t+1) come alive one key block at a time while the
+      // scores of tile t die item by item
+      if constexpr (HN) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int u = 0; u < PF; ++u) ka[u] = kread.read(kn, 16 * (u / NDS), u % NDS);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // K operands are read PF steps ahead of the MFMAs that use them; the
-      // scheduling fences keep each read where it was issued, so LDS latency
-      // hides behind the matrix work instead of stalling it
-      {
-        constexpr int PF = 3, U = NDS * NKB;       // steps: (ds, kb)
-        bf16x8 ka[PF];
-#pragma unroll
-        for (int u = 0; u < PF && u < U; ++u) ka[u] = kread.read(kt, 16 * (u % NKB), u / NKB);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int ds = u / NKB, kb = u % NKB;
+      for (int u = 0; u < US; ++u) {
+        if constexpr (HN) {
+          const int kb = u / NDS, ds = u % NDS;
           const bf16x8 a = ka[u % PF];
-          if (u + PF < U) ka[u % PF] = kread.read(kt, 16 * ((u + PF) % NKB), (u + PF) / NKB);
+          if (u + PF < US) ka[u % PF] = kread.read(kn, 16 * ((u + PF) / NDS), (u + PF) % NDS);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = mfma_bf16(a, qf[qb][ds], s[kb][qb]);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int qb = 0; qb < NQB; ++qb)
+            sn[kb][qb] = mfma_bf16(a, qf[qb][ds], ds == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sn[kb][qb]);
         }
-      }
-      // in-tile mask: key j0 + 16kb + 4g + i is visible iff 16kb + i <= lim
-      if constexpr (decltype(masked)::value) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const int last = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
-          const int lim = last - j0 - 4 * g;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * kb + i > lim) s[kb][qb][i] = kNegInf;
-        }
-      }
-      // online softmax (base 2), per query column
-      float mx[NQB];
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float t = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t = fmaxf(t, s[kb][qb][i]);
-        mx[qb] = wave_max_xor16_32(t) * scale_log2;
-        grow |= !(mx[qb] <= m[qb] + kRescaleSlack);   // also true while m = -inf
-      }
-      // uniform branch (the vote is read into a scalar register)
-      if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const float m_new = fmaxf(m[qb], mx[qb]);
-          const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m[qb] - m_new);
-          m[qb] = m_new;
-          lsum[qb] *= corr;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[db][qb] *= corr;
-        }
-      }
-      bf16x8 pb[NKS][NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float m_use = (m[qb] == kNegInf) ? 0.f : m[qb];   // never (-inf) - (-inf)
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = exp2_fast(__builtin_fmaf(s[kb][qb][i], scale_log2, -m_use));
-            s[kb][qb][i] = p;
-            ps += p;
-          }
-        lsum[qb] += ps;
-#pragma unroll
-        for (int t = 0; t < NKS; ++t) pb[t][qb] = pack_bf16(s[2 * t][qb], s[2 * t + 1][qb]);
-      }
-      // O^T[d][query] += V^T P^T over the tile's keys (V^T read PF steps ahead)
-      {
-        constexpr int PF = 3, U = NKS * NDB;       // steps: (t, db)
-        bf16x8 va[PF];
-#pragma unroll
-        for (int u = 0; u < PF && u < U; ++u)
-          va[u] = cat(vread.read(vt, 32 * (u / NDB), u % NDB), vread.read(vt, 32 * (u / NDB) + 16, u % NDB));
+        for (int e = u * EA / US; e < (u + 1) * EA / US; ++e) p_item(e);
         __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // phase B
+    {
+      constexpr int PF = 3;
+      constexpr int EB = NE - EA;           // probability items left
+      constexpr int HB = UP / 2;            // steps in each PV half
+      bf16x8 va[PF];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int t = u / NDB, db = u % NDB;
-          const bf16x8 a = va[u % PF];
-          if (u + PF < U) {
-            const int t2 = (u + PF) / NDB, db2 = (u + PF) % NDB;
-            va[u % PF] = cat(vread.read(vt, 32 * t2, db2), vread.read(vt, 32 * t2 + 16, db2));
-          }
+      for (int u = 0; u < PF; ++u)
+        va[u] = cat(vread.read(vt, 32 * (u / NDB), u % NDB), vread.read(vt, 32 * (u / NDB) + 16, u % NDB));
+      __builtin_amdgcn_sched_barrier(0);
+      float mx[NQB];
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) acc[db][qb] = mfma_bf16(a, pb[t][qb], acc[db][qb]);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < UP; ++u) {
+        const int h = u / NDB, db = u % NDB;
+        const bf16x8 a = va[u % PF];
+        if (u + PF < UP) {
+          const int h2 = (u + PF) / NDB, db2 = (u + PF) % NDB;
+          va[u % PF] = cat(vread.read(vt, 32 * h2, db2), vread.read(vt, 32 * h2 + 16, db2));
         }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) acc[db][qb] = mfma_bf16(a, pb[h][qb], acc[db][qb]);
+        if (u < HB) {
+#pragma unroll
+          for (int e = EA + u * EB / HB; e < EA + (u + 1) * EB / HB; ++e) p_item(e);
+        } else if constexpr (HN) {
+          // second half: mask (when needed) and row max of the next tile
+          const int v = u - HB;
+          if constexpr (NM) {
+            constexpr int MI = (NQB * NKB + HB - 1) / HB;   // mask items per step
+#pragma unroll
+            for (int w = v * MI; w < (v + 1) * MI && w < NQB * NKB; ++w) mask_item(sn, (t + 1) * BC, w / NKB, w % NKB);
+          } else {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              if (v == (2 * qb + 1) * HB / (2 * NQB)) mx[qb] = row_max(sn, qb);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (HN) {
+        if constexpr (NM) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) mx[qb] = row_max(sn, qb);
+        }
+        update_base(mx);
       }
     }
   };
 
-  // One key tile: prefetch tile j+1 into (kn, vn), compute tile j from (kt, vt).
-  auto tile_step = [&](const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn, int j) __attribute__((always_inline)) {
-    const int j0 = j * BC;
-    if (j + 1 < ntk) {
-      copier.issue(kn, Kh + (size_t)(j0 + BC) * D, n - j0 - BC);
-      copier.issue(vn, Vh + (size_t)(j0 + BC) * D, n - j0 - BC);
-    }
-    // a wave whose rows all precede the tile has nothing to do in it
-    if (!CAUSAL || (j0 <= q0w + QW - 1)) {
-      if ((CAUSAL || RAGGED) && ((CAUSAL && j0 + BC - 1 > q0w) || (j0 + BC > n))) {
-        tile_compute(kt, vt, j0, std::true_type{});
+  // Step t: K(t+1) and V(t) are resident.  Copy K(t+NBUF) and V(t+NBUF-1)
+  // into the buffers that step t-1 finished with, run the pipelined body when
+  // this wave has rows that see tile t, then wait for the copies that step
+  // t+1 needs and synchronise.
+  constexpr int PER = AsyncTileCopy<D, BC, NW>::PER_WAVE;   // copy instructions per tile and wave
+  auto step = [&](f32x4 (&sc)[NKB][NQB], f32x4 (&sn)[NKB][NQB], int t) __attribute__((always_inline)) {
+    const int b0 = t % NBUF, b1 = (t + 1) % NBUF, bl = (t + NBUF - 1) % NBUF;
+    const bool ck = t + NBUF < ntk, cv = t + NBUF - 1 < ntk;
+    if (cv) copier.issue(v_lds[bl], Vh + (size_t)(t + NBUF - 1) * BC * D, n - (t + NBUF - 1) * BC);
+    if (ck) copier.issue(k_lds[b0], Kh + (size_t)(t + NBUF) * BC * D, n - (t + NBUF) * BC);
+    if (t <= last) {
+      const __bf16* kn = k_lds[b1];
+      const __bf16* vt = v_lds[b0];
+      if (t + 1 <= last) {
+        if ((CAUSAL || RAGGED) && tile_masked(t + 1)) {
+          body(sc, sn, kn, vt, t, std::true_type{}, std::true_type{});
+        } else {
+          body(sc, sn, kn, vt, t, std::true_type{}, std::false_type{});
+        }
       } else {
-        tile_compute(kt, vt, j0, std::false_type{});
+        body(sc, sn, kn, vt, t, std::false_type{}, std::false_type{});
       }
     }
-    async_copy_wait();
+    if constexpr (NBUF == 3) {
+      if (ck) async_copy_wait_allbut<2 * PER>();
+      else if (cv) async_copy_wait_allbut<PER>();
+      else async_copy_wait();
+    } else {
+      async_copy_wait();
+    }
     __syncthreads();
   };
 
 #pragma unroll 1
-  for (int j = 0; j < ntk; j += 2) {
-    tile_step(k_lds0, v_lds0, k_lds1, v_lds1, j);
-    if (j + 1 < ntk) tile_step(k_lds1, v_lds1, k_lds0, v_lds0, j + 1);
+  for (int t = 0; t < ntk; t += 2) {
+    step(sa, sb, t);
+    if (t + 1 < ntk) step(sb, sa, t + 1);
   }
 
   // epilogue: O = acc / l, L = (m + log2 l) * ln 2
@@ -266,9 +368,9 @@ static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, v
   const int ntq = (n + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
-  auto kern = causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true>
-            : (n % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true>
-                       : fwd_bf16_kernel<D, QW, NW, BC, false, false>;
+  auto kern = causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true, kFwdBuffers>
+            : (n % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, kFwdBuffers>
+                       : fwd_bf16_kernel<D, QW, NW, BC, false, false, kFwdBuffers>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                      (__bf16*)o, lse, bh, n, sl2);
   return hipGetLastError();
@@ -280,7 +382,6 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            hipStream_t st) {
   if (d == 128 && bm == 128 && bn == 64) return launch_fwd_inst<128, 32, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
   if (d == 128 && bm == 256 && bn == 64) return launch_fwd_inst<128, 32, 8, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
-  if (d == 128 && bm == 128 && bn == 128) return launch_fwd_inst<128, 32, 4, 128>(q, k, v, o, lse, bh, n, scale, causal, st);
   if (d == 64 && bm == 128 && bn == 64) return launch_fwd_inst<64, 32, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
   if (d == 64 && bm == 256 && bn == 64) return launch_fwd_inst<64, 32, 8, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
   return hipErrorInvalidValue;

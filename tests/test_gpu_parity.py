@@ -126,7 +126,7 @@ def test_bf16_2048_d64_noncausal():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("fwd_tiles", [(128, 64), (256, 64), (128, 128)])
+@pytest.mark.parametrize("fwd_tiles", [(128, 64), (256, 64)])
 def test_bf16_d128_small(causal, fwd_tiles):
     arrays = make_inputs(4, 1024, 128, seed=2)
     g = run_gpu(arrays, "bf16", causal, fwd_tiles)
