@@ -30,3 +30,4 @@ from ._lib import (  # noqa: F401
     forward,
     load_library,
 )
+from .autograd import FlashAttention, flash_attention  # noqa: F401

@@ -1,0 +1,62 @@
+"""torch autograd drop-in for exact tiled attention.
+
+``flash_attention(q, k, v, causal=False, scale=None)`` computes
+``softmax(scale * q k^T) v`` (keys after the query masked when ``causal``)
+with the library's kernels and differentiates through them.  Following
+"Assignment2: FlashAttention & Distributed Data Parallel notes" (CS336)
+section 1.2, the forward saves only Q, K, V, O and the logsumexp L (one
+float per row, no N x N matrix); section 1.4's backward then runs
+``fa_bwd_preprocess`` (D = rowsum(O * dO)), ``fa_bwd_dkdv`` and ``fa_bwd_dq``
+on the current stream.
+
+Inputs are device tensors of one dtype (float32 or bfloat16) and shape
+``[..., n, d]`` with equal shapes for q, k and v; the leading dimensions are
+flattened into the kernels' head axis.  Gradients come back in the input
+dtype.  There is no fallback: the kernels run or the call raises.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _flat(t: torch.Tensor) -> torch.Tensor:
+    return t.reshape(-1, t.shape[-2], t.shape[-1]).contiguous()
+
+
+class FlashAttention(torch.autograd.Function):
+    """Autograd function over ``fa_fwd`` and the three backward calls."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal: bool, scale: float | None):
+        if not (q.shape == k.shape == v.shape):
+            raise ValueError(f"q, k, v must have one shape, got {tuple(q.shape)}, "
+                             f"{tuple(k.shape)}, {tuple(v.shape)}")
+        if q.dim() < 3:
+            raise ValueError(f"expected [..., n, d] tensors, got shape {tuple(q.shape)}")
+        shape = q.shape
+        q3, k3, v3 = _flat(q), _flat(k), _flat(v)
+        o, lse = _lib.forward(q3, k3, v3, causal, scale)
+        ctx.save_for_backward(q3, k3, v3, o, lse)
+        ctx.causal = bool(causal)
+        ctx.scale = scale
+        ctx.shape = shape
+        return o.view(shape)
+
+    @staticmethod
+    def backward(ctx, do):
+        q3, k3, v3, o, lse = ctx.saved_tensors
+        do3 = do.to(o.dtype).reshape(o.shape).contiguous()
+        dq, dk, dv, _ = _lib.backward(q3, k3, v3, o, do3, lse, ctx.causal, ctx.scale)
+        shape = ctx.shape
+        return dq.view(shape), dk.view(shape), dv.view(shape), None, None
+
+
+def flash_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                    scale: float | None = None) -> torch.Tensor:
+    """Exact attention with the library's kernels; differentiable in q, k, v.
+
+    ``scale`` defaults to 1/sqrt(d) and must be finite and positive."""
+    return FlashAttention.apply(q, k, v, causal, scale)

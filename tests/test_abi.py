@@ -168,3 +168,14 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 16, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q, causal=True)
+
+
+def test_autograd_op_validates_on_host():
+    import torch
+    q = torch.zeros(2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.flash_attention(q, q, q)                      # host tensors are refused
+    with pytest.raises(ValueError):
+        fa.flash_attention(q, q[:, :8], q[:, :8])        # shapes must agree
+    with pytest.raises(ValueError):
+        fa.flash_attention(q[0, 0], q[0, 0], q[0, 0])    # needs [..., n, d]
