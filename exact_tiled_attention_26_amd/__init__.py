@@ -23,9 +23,12 @@ from ._lib import (  # noqa: F401
     fa_abi_version,
     fa_bwd_dkdv,
     fa_bwd_dq,
+    fa_bwd_dq_rect,
+    fa_bwd_dkdv_rect,
     fa_bwd_preprocess,
     fa_default_tiles,
     fa_fwd,
+    fa_fwd_rect,
     fa_status_str,
     forward,
     load_library,

@@ -27,6 +27,9 @@ SIGNATURES = {
     "fa_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
     "fa_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P],
     "fa_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P],
+    "fa_fwd_rect": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P],
+    "fa_bwd_dkdv_rect": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P],
+    "fa_bwd_dq_rect": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P],
     "fa_default_tiles": [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "fa_status_str": [_I],
     "fa_abi_version": [],
@@ -112,14 +115,19 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def _check_io(ref, tensors, name_dtype):
+def _check_io(ref, tensors, name_dtype, kref=None):
+    """Device, contiguity, dtype and shape checks: "io" tensors match ref (q),
+    "kv" tensors match kref (k; default ref) in shape and ref in dtype, "row"
+    tensors are float32 [bh, n] with ref's bh and n."""
     import torch
+    kref = ref if kref is None else kref
     for name, t, want in tensors:
         _require(t.is_cuda, f"{name} must be a device tensor")
         _require(t.is_contiguous(), f"{name} must be contiguous")
-        if want == "io":
-            _require(t.dtype == ref.dtype and tuple(t.shape) == tuple(ref.shape),
-                     f"{name} must match q in dtype and shape")
+        if want in ("io", "kv"):
+            shape = ref.shape if want == "io" else kref.shape
+            _require(t.dtype == ref.dtype and tuple(t.shape) == tuple(shape),
+                     f"{name} must match {'q' if want == 'io' else 'k'} in shape and q in dtype")
         else:
             _require(t.dtype == torch.float32 and tuple(t.shape) == tuple(ref.shape[:2]),
                      f"{name} must be float32 of shape [bh, n]")
@@ -175,13 +183,65 @@ def fa_bwd_dq(q, k, v, dO, lse, delta, dq, causal: bool, scale: float | None = N
     _check("fa_bwd_dq", st)
 
 
+def _kv_shape(q, k):
+    bh, _, d = _shape3(q)
+    bhk, nk, dk = _shape3(k)
+    _require(bhk == bh and dk == d, "k must be [bh, nk, d] with q's bh and d")
+    return nk
+
+
+def fa_fwd_rect(q, k, v, o, lse, causal: bool, scale: float | None = None,
+                block_m: int = 0, block_n: int = 0, stream=None):
+    """Forward for q [bh, nq, d] against k, v [bh, nk, d]; causal masking is
+    aligned to the end of the keys (see include/fa.h)."""
+    bh, nq, d = _shape3(q)
+    nk = _kv_shape(q, k)
+    _check_io(q, [("q", q, "io"), ("k", k, "kv"), ("v", v, "kv"), ("o", o, "io"), ("lse", lse, "row")],
+              None, kref=k)
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), bh, nq, nk, d,
+                                    _dtype_code(q), scale, int(bool(causal)), int(block_m), int(block_n),
+                                    _stream(stream))
+    _check("fa_fwd_rect", st)
+
+
+def fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, causal: bool, scale: float | None = None,
+                     block_m: int = 0, block_n: int = 0, stream=None):
+    """dK, dV for q, dO [bh, nq, d] against k, v [bh, nk, d]."""
+    bh, nq, d = _shape3(q)
+    nk = _kv_shape(q, k)
+    _check_io(q, [("q", q, "io"), ("k", k, "kv"), ("v", v, "kv"), ("dO", dO, "io"), ("lse", lse, "row"),
+                  ("delta", delta, "row"), ("dk", dk, "kv"), ("dv", dv, "kv")], None, kref=k)
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_dkdv_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
+                                         _ptr(dk), _ptr(dv), bh, nq, nk, d, _dtype_code(q), scale,
+                                         int(bool(causal)), int(block_m), int(block_n), _stream(stream))
+    _check("fa_bwd_dkdv_rect", st)
+
+
+def fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, causal: bool, scale: float | None = None,
+                   block_m: int = 0, block_n: int = 0, stream=None):
+    """dQ for q, dO [bh, nq, d] against k, v [bh, nk, d]."""
+    bh, nq, d = _shape3(q)
+    nk = _kv_shape(q, k)
+    _check_io(q, [("q", q, "io"), ("k", k, "kv"), ("v", v, "kv"), ("dO", dO, "io"), ("lse", lse, "row"),
+                  ("delta", delta, "row"), ("dq", dq, "io")], None, kref=k)
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_dq_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
+                                       _ptr(dq), bh, nq, nk, d, _dtype_code(q), scale, int(bool(causal)),
+                                       int(block_m), int(block_n), _stream(stream))
+    _check("fa_bwd_dq_rect", st)
+
+
 # ------------------------------------------------------------------ allocating helpers
 def forward(q, k, v, causal: bool, scale=None, block_m=0, block_n=0, stream=None):
-    """Allocate O and L with torch and run fa_fwd; returns (o, lse)."""
+    """Allocate O and L with torch and run fa_fwd (fa_fwd_rect when k has a
+    different length than q); returns (o, lse)."""
     import torch
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, causal, scale, block_m, block_n, stream)
+    fwd = fa_fwd if tuple(k.shape) == tuple(q.shape) else fa_fwd_rect
+    fwd(q, k, v, o, lse, causal, scale, block_m, block_n, stream)
     return o, lse
 
 
@@ -192,7 +252,10 @@ def backward(q, k, v, o, dO, lse, causal: bool, scale=None, tiles_dkdv=(0, 0), t
     import torch
     delta = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    square = tuple(k.shape) == tuple(q.shape)
     fa_bwd_preprocess(o, dO, delta, stream)
-    fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, causal, scale, *tiles_dkdv, stream=stream)
-    fa_bwd_dq(q, k, v, dO, lse, delta, dq, causal, scale, *tiles_dq, stream=stream)
+    (fa_bwd_dkdv if square else fa_bwd_dkdv_rect)(q, k, v, dO, lse, delta, dk, dv, causal, scale,
+                                                  *tiles_dkdv, stream=stream)
+    (fa_bwd_dq if square else fa_bwd_dq_rect)(q, k, v, dO, lse, delta, dq, causal, scale, *tiles_dq,
+                                              stream=stream)
     return dq, dk, dv, delta

@@ -9,10 +9,13 @@ float per row, no N x N matrix); section 1.4's backward then runs
 ``fa_bwd_preprocess`` (D = rowsum(O * dO)), ``fa_bwd_dkdv`` and ``fa_bwd_dq``
 on the current stream.
 
-Inputs are device tensors of one dtype (float32 or bfloat16) and shape
-``[..., n, d]`` with equal shapes for q, k and v; the leading dimensions are
-flattened into the kernels' head axis.  Gradients come back in the input
-dtype.  There is no fallback: the kernels run or the call raises.
+Inputs are device tensors of one dtype (float32 or bfloat16): q of shape
+``[..., nq, d]`` and k, v of shape ``[..., nk, d]`` with the same leading
+dimensions, which are flattened into the kernels' head axis.  With nq != nk
+the causal mask is aligned to the end of the keys (query i sees keys
+0 .. i + nk - nq, e.g. new tokens against a key/value cache).  Gradients
+come back in the input dtype.  There is no fallback: the kernels run or the
+call raises.
 """
 
 from __future__ import annotations
@@ -31,27 +34,26 @@ class FlashAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, causal: bool, scale: float | None):
-        if not (q.shape == k.shape == v.shape):
-            raise ValueError(f"q, k, v must have one shape, got {tuple(q.shape)}, "
-                             f"{tuple(k.shape)}, {tuple(v.shape)}")
-        if q.dim() < 3:
-            raise ValueError(f"expected [..., n, d] tensors, got shape {tuple(q.shape)}")
-        shape = q.shape
+        if q.dim() < 3 or k.dim() != q.dim():
+            raise ValueError(f"expected [..., n, d] tensors, got shapes {tuple(q.shape)}, {tuple(k.shape)}")
+        if k.shape != v.shape or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != q.shape[-1]:
+            raise ValueError(f"k and v must be [..., nk, d] with q's leading dims and d, got "
+                             f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
         q3, k3, v3 = _flat(q), _flat(k), _flat(v)
         o, lse = _lib.forward(q3, k3, v3, causal, scale)
         ctx.save_for_backward(q3, k3, v3, o, lse)
         ctx.causal = bool(causal)
         ctx.scale = scale
-        ctx.shape = shape
-        return o.view(shape)
+        ctx.shapes = (q.shape, k.shape)
+        return o.view(q.shape)
 
     @staticmethod
     def backward(ctx, do):
         q3, k3, v3, o, lse = ctx.saved_tensors
         do3 = do.to(o.dtype).reshape(o.shape).contiguous()
         dq, dk, dv, _ = _lib.backward(q3, k3, v3, o, do3, lse, ctx.causal, ctx.scale)
-        shape = ctx.shape
-        return dq.view(shape), dk.view(shape), dv.view(shape), None, None
+        qshape, kshape = ctx.shapes
+        return dq.view(qshape), dk.view(kshape), dv.view(kshape), None, None
 
 
 def flash_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,

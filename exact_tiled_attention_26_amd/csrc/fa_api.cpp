@@ -54,11 +54,21 @@ fa_status resolve_tiles(fa_dtype dtype, int kernel, int d, int& bm, int& bn) {
   return FA_OK;
 }
 
-fa_status check_common(int bh, int n, int d, fa_dtype dtype) {
+fa_status check_common(int bh, int nq, int nk, int d, fa_dtype dtype) {
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
-  if (bh < 0 || n < 0 || d <= 0) return FA_ERR_INVALID_ARG;
-  if (n > kMaxN || bh > kMaxBH) return FA_ERR_UNSUPPORTED;
+  if (bh < 0 || nq < 0 || nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (nq > kMaxN || nk > kMaxN || bh > kMaxBH) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_F32 ? !f32_head_dim_ok(d) : !bf16_head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// Query/key lengths of an attention call: sets `empty` for a no-op call;
+// rejects rows without keys (one length zero, or causal with nq > nk).
+fa_status check_lengths(int bh, int nq, int nk, int causal, bool& empty) {
+  empty = bh == 0 || (nq == 0 && nk == 0);
+  if (empty) return FA_OK;
+  if (nq == 0 || nk == 0) return FA_ERR_INVALID_ARG;
+  if (causal && nq > nk) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -123,30 +133,38 @@ fa_status fa_default_tiles(fa_dtype dtype, int d, int kernel, int* block_m, int*
   return FA_OK;
 }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int bh, int n, int d, fa_dtype dtype, float scale, int causal,
-                 int block_m, int block_n, void* stream) {
-  fa_status s = check_common(bh, n, d, dtype);
+fa_status fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int bh, int nq, int nk, int d, fa_dtype dtype, float scale, int causal,
+                      int block_m, int block_n, void* stream) {
+  fa_status s = check_common(bh, nq, nk, d, dtype);
   if (s != FA_OK) return s;
   if ((s = check_scale(scale)) != FA_OK) return s;
   if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
   if ((s = resolve_tiles(dtype, kFwd, d, block_m, block_n)) != FA_OK) return s;
-  if (bh == 0 || n == 0) return FA_OK;
-  if ((s = check_grid(bh, n, block_m)) != FA_OK) return s;
+  bool empty = false;
+  if ((s = check_lengths(bh, nq, nk, causal, empty)) != FA_OK || empty) return s;
+  if ((s = check_grid(bh, nq, block_m)) != FA_OK) return s;
   if ((s = check_ptrs(q, k, v, o, lse)) != FA_OK) return s;
   if (any_equal({o, lse}, {q, k, v, o, lse})) return FA_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == FA_BF16)
-    return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, bh, n, d, scale, causal != 0,
+    return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, bh, nq, nk, d, scale, causal != 0,
                                         block_m, block_n, st));
   return from_hip(fa::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v,
-                                     (float*)o, lse, bh, n, d, scale, causal != 0, block_m,
+                                     (float*)o, lse, bh, nq, nk, d, scale, causal != 0, block_m,
                                      block_n, st));
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int bh, int n, int d, fa_dtype dtype, float scale, int causal,
+                 int block_m, int block_n, void* stream) {
+  return fa_fwd_rect(q, k, v, o, lse, bh, n, n, d, dtype, scale, causal, block_m, block_n,
+                     stream);
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dO, float* delta,
                             int bh, int n, int d, fa_dtype dtype, void* stream) {
-  fa_status s = check_common(bh, n, d, dtype);
+  fa_status s = check_common(bh, n, n, d, dtype);
   if (s != FA_OK) return s;
   if (bh == 0 || n == 0) return FA_OK;
   if ((s = check_grid(bh, n, 8)) != FA_OK) return s;  // 8+ rows per block
@@ -156,48 +174,66 @@ fa_status fa_bwd_preprocess(const void* o, const void* dO, float* delta,
                                         static_cast<hipStream_t>(stream)));
 }
 
-fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                      const float* lse, const float* delta, void* dk, void* dv,
-                      int bh, int n, int d, fa_dtype dtype, float scale, int causal,
-                      int block_m, int block_n, void* stream) {
-  fa_status s = check_common(bh, n, d, dtype);
+fa_status fa_bwd_dkdv_rect(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lse, const float* delta, void* dk, void* dv,
+                           int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
+                           int causal, int block_m, int block_n, void* stream) {
+  fa_status s = check_common(bh, nq, nk, d, dtype);
   if (s != FA_OK) return s;
   if ((s = check_scale(scale)) != FA_OK) return s;
   if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
   if ((s = resolve_tiles(dtype, kDkdv, d, block_m, block_n)) != FA_OK) return s;
-  if (bh == 0 || n == 0) return FA_OK;
-  if ((s = check_grid(bh, n, block_n)) != FA_OK) return s;
+  bool empty = false;
+  if ((s = check_lengths(bh, nq, nk, causal, empty)) != FA_OK || empty) return s;
+  if ((s = check_grid(bh, nk, block_n)) != FA_OK) return s;
   if ((s = check_ptrs(q, k, v, dO, lse, delta, dk, dv)) != FA_OK) return s;
   if (any_equal({dk, dv}, {q, k, v, dO, lse, delta, dk, dv})) return FA_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == FA_BF16)
-    return from_hip(fa::launch_dkdv_bf16(q, k, v, dO, lse, delta, dk, dv, bh, n, d, scale,
+    return from_hip(fa::launch_dkdv_bf16(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, d, scale,
                                          causal != 0, block_m, block_n, st));
   return from_hip(fa::launch_dkdv_f32((const float*)q, (const float*)k, (const float*)v,
                                       (const float*)dO, lse, delta, (float*)dk, (float*)dv, bh,
-                                      n, d, scale, causal != 0, block_m, block_n, st));
+                                      nq, nk, d, scale, causal != 0, block_m, block_n, st));
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                      const float* lse, const float* delta, void* dk, void* dv,
+                      int bh, int n, int d, fa_dtype dtype, float scale, int causal,
+                      int block_m, int block_n, void* stream) {
+  return fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, bh, n, n, d, dtype, scale, causal,
+                          block_m, block_n, stream);
+}
+
+fa_status fa_bwd_dq_rect(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* delta, void* dq,
+                         int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
+                         int causal, int block_m, int block_n, void* stream) {
+  fa_status s = check_common(bh, nq, nk, d, dtype);
+  if (s != FA_OK) return s;
+  if ((s = check_scale(scale)) != FA_OK) return s;
+  if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
+  if ((s = resolve_tiles(dtype, kDq, d, block_m, block_n)) != FA_OK) return s;
+  bool empty = false;
+  if ((s = check_lengths(bh, nq, nk, causal, empty)) != FA_OK || empty) return s;
+  if ((s = check_grid(bh, nq, block_m)) != FA_OK) return s;
+  if ((s = check_ptrs(q, k, v, dO, lse, delta, dq)) != FA_OK) return s;
+  if (any_equal({dq}, {q, k, v, dO, lse, delta, dq})) return FA_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == FA_BF16)
+    return from_hip(fa::launch_dq_bf16(q, k, v, dO, lse, delta, dq, bh, nq, nk, d, scale,
+                                       causal != 0, block_m, block_n, st));
+  return from_hip(fa::launch_dq_f32((const float*)q, (const float*)k, (const float*)v,
+                                    (const float*)dO, lse, delta, (float*)dq, bh, nq, nk, d,
+                                    scale, causal != 0, block_m, block_n, st));
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                     const float* lse, const float* delta, void* dq,
                     int bh, int n, int d, fa_dtype dtype, float scale, int causal,
                     int block_m, int block_n, void* stream) {
-  fa_status s = check_common(bh, n, d, dtype);
-  if (s != FA_OK) return s;
-  if ((s = check_scale(scale)) != FA_OK) return s;
-  if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
-  if ((s = resolve_tiles(dtype, kDq, d, block_m, block_n)) != FA_OK) return s;
-  if (bh == 0 || n == 0) return FA_OK;
-  if ((s = check_grid(bh, n, block_m)) != FA_OK) return s;
-  if ((s = check_ptrs(q, k, v, dO, lse, delta, dq)) != FA_OK) return s;
-  if (any_equal({dq}, {q, k, v, dO, lse, delta, dq})) return FA_ERR_INVALID_ARG;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == FA_BF16)
-    return from_hip(fa::launch_dq_bf16(q, k, v, dO, lse, delta, dq, bh, n, d, scale,
-                                       causal != 0, block_m, block_n, st));
-  return from_hip(fa::launch_dq_f32((const float*)q, (const float*)k, (const float*)v,
-                                    (const float*)dO, lse, delta, (float*)dq, bh, n, d, scale,
-                                    causal != 0, block_m, block_n, st));
+  return fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, bh, n, n, d, dtype, scale, causal,
+                        block_m, block_n, stream);
 }
 
 }  // extern "C"

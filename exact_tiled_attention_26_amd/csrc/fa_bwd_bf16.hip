@@ -32,27 +32,29 @@ namespace fa {
 
 // Asynchronous copy of BR consecutive fp32 row values (L or D) of one head
 // into LDS with global_load_lds_dword (lane i -> LDS float i).  Rows at or past
-// n re-read row n - 1; the kernels mask those rows.
+// nrows re-read row nrows - 1; the kernels mask those rows.
 template <int BR>
-__device__ __forceinline__ void rows_load_async(float* lds, const float* src, int i0, int n,
+__device__ __forceinline__ void rows_load_async(float* lds, const float* src, int i0, int nrows,
                                                 int lane) {
   static_assert(BR % 64 == 0, "one dword per lane");
 #pragma unroll
   for (int k = 0; k < BR / 64; ++k) {
-    const int r = min(i0 + 64 * k + lane, n - 1);
+    const int r = min(i0 + 64 * k + lane, nrows - 1);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + r),
                                      (__attribute__((address_space(3))) void*)(lds + 64 * k), 4, 0, 0);
   }
 }
 
-// RAGGED: n may not be a multiple of BR (the last query tile needs the mask).
+// nq query rows attend to nk key rows; causal masking is aligned to the end
+// of the key sequence (query i sees keys 0 .. i + nk - nq).
+// RAGGED: nq may not be a multiple of BR (the last query tile needs the mask).
 template <int D, int KW, int NW, int BR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(NW * 64, 1)
 void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ DELTA,
                       __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                      int bh, int n, float scale, float scale_log2) {
+                      int bh, int nq, int nk, float scale, float scale_log2) {
   constexpr int BC = KW * NW;
   constexpr int NKB = KW / 16;   // 16-key blocks per wave
   constexpr int NDS = D / 32;
@@ -72,21 +74,22 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int kt = blockIdx.x / bh;          // causal: tile 0 sees the most queries
   const int k0 = kt * BC;
   const int k0w = k0 + wave * KW;
-  const size_t hoff = (size_t)head * n * D;
-  const __bf16* Qh = Q + hoff;
-  const __bf16* dOh = dO + hoff;
-  const float* Lh = LSE + (size_t)head * n;
-  const float* Dh = DELTA + (size_t)head * n;
+  const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
+  const __bf16* Qh = Q + hoffq;
+  const __bf16* dOh = dO + hoffq;
+  const float* Lh = LSE + (size_t)head * nq;
+  const float* Dh = DELTA + (size_t)head * nq;
 
-  const int ntq = (n + BR - 1) / BR;
-  const int it0 = CAUSAL ? (k0 / BR) : 0;   // earlier query rows see none of these keys
+  const int ntq = (nq + BR - 1) / BR;
+  const int it0 = CAUSAL ? max(0, k0 - off) / BR : 0;   // earlier query rows see none of these keys
   // compiler-visible copies: measured faster than the hidden form here
   const AsyncTileCopy<D, BR, NW, false> copier(wave, lane);
   auto issue_tile = [&](__bf16* qd, __bf16* od, float* ld, float* dd, int i0) __attribute__((always_inline)) {
-    copier.issue(qd, Qh + (size_t)i0 * D, n - i0);
-    copier.issue(od, dOh + (size_t)i0 * D, n - i0);
-    if (wave == 0) rows_load_async<BR>(ld, Lh, i0, n, lane);
-    if (wave == 1) rows_load_async<BR>(dd, Dh, i0, n, lane);
+    copier.issue(qd, Qh + (size_t)i0 * D, nq - i0);
+    copier.issue(od, dOh + (size_t)i0 * D, nq - i0);
+    if (wave == 0) rows_load_async<BR>(ld, Lh, i0, nq, lane);
+    if (wave == 1) rows_load_async<BR>(dd, Dh, i0, nq, lane);
   };
   issue_tile(q_lds0, o_lds0, l_lds0, d_lds0, it0 * BR);
 
@@ -98,9 +101,9 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     const int key = k0w + 16 * kb + l16;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      if (key < n) {
-        kf[kb][ds] = *reinterpret_cast<const bf16x8*>(K + hoff + (size_t)key * D + 32 * ds + 8 * g);
-        vf[kb][ds] = *reinterpret_cast<const bf16x8*>(V + hoff + (size_t)key * D + 32 * ds + 8 * g);
+      if (key < nk) {
+        kf[kb][ds] = *reinterpret_cast<const bf16x8*>(K + hoffk + (size_t)key * D + 32 * ds + 8 * g);
+        vf[kb][ds] = *reinterpret_cast<const bf16x8*>(V + hoffk + (size_t)key * D + 32 * ds + 8 * g);
       } else {
         kf[kb][ds] = bf16x8{};
         vf[kb][ds] = bf16x8{};
@@ -162,7 +165,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     e.pv[h][kb][i] = p;
     e.dsv[h][kb][i] = p * (dp[h][kb][i] - e.dd[h][i]);
   };
-  // Masked entries (key after query, or query past n) get P = dS = 0.  Only
+  // Masked entries (key after query + off, or query past nq) get P = dS = 0.  Only
   // tiles crossing the diagonal or the end of the sequence run this, behind
   // a uniform branch, so the other tiles carry no mask arithmetic.
   auto ew_mask = [&](int i0, int t, EwState& e) __attribute__((always_inline)) {
@@ -171,7 +174,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = i0 + 32 * t + 16 * h + 4 * g + i;
-        const int lim = (q < n) ? (CAUSAL ? q - k0w - l16 : 0x7fffffff) : -1;
+        const int lim = (q < nq) ? (CAUSAL ? q + off - k0w - l16 : 0x7fffffff) : -1;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           if (16 * kb > lim) {
@@ -302,11 +305,11 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                        __bf16* qn, __bf16* on, float* ln, float* dn, int it) __attribute__((always_inline)) {
     const int i0 = it * BR;
     if (it + 1 < ntq) issue_tile(qn, on, ln, dn, i0 + BR);
-    const bool active = !CAUSAL || (i0 + BR - 1 >= k0w);
+    const bool active = !CAUSAL || (i0 + BR - 1 + off >= k0w);
     if (active) {
       // only tiles crossing the diagonal or the end of the sequence are masked;
       // they run a separate copy so that the others carry no mask arithmetic
-      if ((CAUSAL || RAGGED) && ((CAUSAL && i0 < k0w + KW - 1) || (i0 + BR > n))) {
+      if ((CAUSAL || RAGGED) && ((CAUSAL && i0 + off < k0w + KW - 1) || (i0 + BR > nq))) {
         run_tile(qt, ot, lt, dt, i0, std::true_type{});
       } else {
         run_tile(qt, ot, lt, dt, i0, std::false_type{});
@@ -326,7 +329,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const int key = k0w + 16 * kb + l16;
-    if (key < n && key < k0 + BC) {
+    if (key < nk && key < k0 + BC) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         bf16x4 k4, v4;
@@ -335,8 +338,8 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           k4[i] = (__bf16)(dk[db][kb][i] * scale);
           v4[i] = (__bf16)dv[db][kb][i];
         }
-        *reinterpret_cast<bf16x4*>(dK + hoff + (size_t)key * D + 16 * db + 4 * g) = k4;
-        *reinterpret_cast<bf16x4*>(dV + hoff + (size_t)key * D + 16 * db + 4 * g) = v4;
+        *reinterpret_cast<bf16x4*>(dK + hoffk + (size_t)key * D + 16 * db + 4 * g) = k4;
+        *reinterpret_cast<bf16x4*>(dV + hoffk + (size_t)key * D + 16 * db + 4 * g) = v4;
       }
     }
   }
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(NW * 64, 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                     const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                    __bf16* __restrict__ dQ, int bh, int n, float scale, float scale_log2) {
+                    __bf16* __restrict__ dQ, int bh, int nq, int nk, float scale, float scale_log2) {
   constexpr int BR = QW * NW;
   constexpr int NQB = QW / 16;
   constexpr int NKB = BC / 16;
@@ -361,21 +364,22 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int ntq = (n + BR - 1) / BR;
+  const int ntq = (nq + BR - 1) / BR;
   const int head = blockIdx.x % bh;
   const int qt = ntq - 1 - blockIdx.x / bh;
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
-  const size_t hoff = (size_t)head * n * D;
-  const __bf16* Kh = K + hoff;
-  const __bf16* Vh = V + hoff;
+  const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const size_t hoffq = (size_t)head * nq * D;
+  const __bf16* Kh = K + (size_t)head * nk * D;
+  const __bf16* Vh = V + (size_t)head * nk * D;
 
-  const int kend = CAUSAL ? min(n, q0 + BR) : n;
+  const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
   const int ntk = (kend + BC - 1) / BC;
   // compiler-visible copies: measured faster than the hidden form here
   const AsyncTileCopy<D, BC, NW, false> copier(wave, lane);
-  copier.issue(k_lds0, Kh, min(BC, n));
-  copier.issue(v_lds0, Vh, min(BC, n));
+  copier.issue(k_lds0, Kh, min(BC, nk));
+  copier.issue(v_lds0, Vh, min(BC, nk));
 
   bf16x8 qf[NQB][NDS], of[NQB][NDS];
   float l2q[NQB], dq_d[NQB];
@@ -384,16 +388,16 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int row = q0w + 16 * qb + l16;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      if (row < n) {
-        qf[qb][ds] = *reinterpret_cast<const bf16x8*>(Q + hoff + (size_t)row * D + 32 * ds + 8 * g);
-        of[qb][ds] = *reinterpret_cast<const bf16x8*>(dO + hoff + (size_t)row * D + 32 * ds + 8 * g);
+      if (row < nq) {
+        qf[qb][ds] = *reinterpret_cast<const bf16x8*>(Q + hoffq + (size_t)row * D + 32 * ds + 8 * g);
+        of[qb][ds] = *reinterpret_cast<const bf16x8*>(dO + hoffq + (size_t)row * D + 32 * ds + 8 * g);
       } else {
         qf[qb][ds] = bf16x8{};
         of[qb][ds] = bf16x8{};
       }
     }
-    l2q[qb] = (row < n) ? LSE[(size_t)head * n + row] * kLog2e : __builtin_inff();
-    dq_d[qb] = (row < n) ? DELTA[(size_t)head * n + row] : 0.f;
+    l2q[qb] = (row < nq) ? LSE[(size_t)head * nq + row] * kLog2e : __builtin_inff();
+    dq_d[qb] = (row < nq) ? DELTA[(size_t)head * nq + row] : 0.f;
   }
 
   // dQ^T accumulator: lane holds d = 16db + 4g + i, query 16qb + l16
@@ -411,10 +415,10 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto tile_step = [&](const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn, int j) __attribute__((always_inline)) {
     const int j0 = j * BC;
     if (j + 1 < ntk) {
-      copier.issue(kn, Kh + (size_t)(j0 + BC) * D, n - j0 - BC);
-      copier.issue(vn, Vh + (size_t)(j0 + BC) * D, n - j0 - BC);
+      copier.issue(kn, Kh + (size_t)(j0 + BC) * D, nk - j0 - BC);
+      copier.issue(vn, Vh + (size_t)(j0 + BC) * D, nk - j0 - BC);
     }
-    const bool active = !CAUSAL || (j0 <= q0w + QW - 1);
+    const bool active = !CAUSAL || (j0 <= q0w + QW - 1 + off);
     if (active) {
       // S^T = K Q^T, dP^T = V dO^T: lane holds key 16kb + 4g + i, query 16qb + l16
       f32x4 s[NKB][NQB], dp[NKB][NQB];
@@ -451,7 +455,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool need_mask = (CAUSAL && j0 + BC - 1 > q0w) || (j0 + BC > n);
+      const bool need_mask = (CAUSAL && j0 + BC - 1 > q0w + off) || (j0 + BC > nk);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -466,7 +470,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       if (need_mask) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          const int last = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
+          const int last = CAUSAL ? min(q0w + 16 * qb + l16 + off, nk - 1) : nk - 1;
           const int lim = last - j0 - 4 * g;   // key j0 + 16kb + 4g + i visible iff 16kb + i <= lim
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
@@ -514,13 +518,13 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int row = q0w + 16 * qb + l16;
-    if (row < n) {
+    if (row < nq) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         bf16x4 q4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) q4[i] = (__bf16)(acc[db][qb][i] * scale);
-        *reinterpret_cast<bf16x4*>(dQ + hoff + (size_t)row * D + 16 * db + 4 * g) = q4;
+        *reinterpret_cast<bf16x4*>(dQ + hoffq + (size_t)row * D + 16 * db + 4 * g) = q4;
       }
     }
   }
@@ -529,37 +533,37 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 template <int D, int KW, int NW, int BR>
 static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, const void* dO,
                                    const float* lse, const float* delta, void* dk, void* dv,
-                                   int bh, int n, float scale, int causal, hipStream_t st) {
+                                   int bh, int nq, int nk, float scale, int causal, hipStream_t st) {
   constexpr int BC = KW * NW;
-  const int ntk = (n + BC - 1) / BC;
+  const int ntk = (nk + BC - 1) / BC;
   const dim3 grid((unsigned)(ntk * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
-  // the non-causal kernel keeps its masked copy even when n is a multiple of
+  // the non-causal kernel keeps its masked copy even when nq is a multiple of
   // BR: the uniform branch around it splits the tile into scheduling regions
   // small enough to stay within the register file
   auto kern = causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true>
                      : dkdv_bf16_kernel<D, KW, NW, BR, false, true>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, bh, n, scale, sl2);
+                     (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, bh, nq, nk, scale, sl2);
   return hipGetLastError();
 }
 
 template <int D, int QW, int NW, int BC>
 static hipError_t launch_dq_inst(const void* q, const void* k, const void* v, const void* dO,
                                  const float* lse, const float* delta, void* dq,
-                                 int bh, int n, float scale, int causal, hipStream_t st) {
+                                 int bh, int nq, int nk, float scale, int causal, hipStream_t st) {
   constexpr int BR = QW * NW;
-  const int ntq = (n + BR - 1) / BR;
+  const int ntq = (nq + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
   if (causal) {
     hipLaunchKernelGGL((dq_bf16_kernel<D, QW, NW, BC, true>), grid, block, 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dq, bh, n, scale, sl2);
+                       lse, delta, (__bf16*)dq, bh, nq, nk, scale, sl2);
   } else {
     hipLaunchKernelGGL((dq_bf16_kernel<D, QW, NW, BC, false>), grid, block, 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dq, bh, n, scale, sl2);
+                       lse, delta, (__bf16*)dq, bh, nq, nk, scale, sl2);
   }
   return hipGetLastError();
 }
@@ -567,26 +571,26 @@ static hipError_t launch_dq_inst(const void* q, const void* k, const void* v, co
 // dK/dV tilings: block_m = query rows per inner step, block_n = keys per workgroup.
 hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO,
                             const float* lse, const float* delta, void* dk, void* dv,
-                            int bh, int n, int d, float scale, int causal, int bm, int bn,
+                            int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                             hipStream_t st) {
   if (d == 128 && bm == 64 && bn == 128)
-    return launch_dkdv_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, n, scale, causal, st);
+    return launch_dkdv_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, st);
   if (d == 128 && bm == 128 && bn == 128)
-    return launch_dkdv_inst<128, 32, 4, 128>(q, k, v, dO, lse, delta, dk, dv, bh, n, scale, causal, st);
+    return launch_dkdv_inst<128, 32, 4, 128>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, st);
   if (d == 64 && bm == 64 && bn == 128)
-    return launch_dkdv_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, n, scale, causal, st);
+    return launch_dkdv_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, st);
   return hipErrorInvalidValue;
 }
 
 // dQ tilings: block_m = queries per workgroup, block_n = keys per inner step.
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO,
                           const float* lse, const float* delta, void* dq,
-                          int bh, int n, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                           hipStream_t st) {
   if (d == 128 && bm == 128 && bn == 64)
-    return launch_dq_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, n, scale, causal, st);
+    return launch_dq_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, st);
   if (d == 64 && bm == 128 && bn == 64)
-    return launch_dq_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, n, scale, causal, st);
+    return launch_dq_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, st);
   return hipErrorInvalidValue;
 }
 

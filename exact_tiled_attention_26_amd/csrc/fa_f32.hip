@@ -33,7 +33,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512)
 void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                     const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-                    int bh, int n, float scale_log2, int BR, int BC) {
+                    int bh, int nq, int nk, float scale_log2, int BR, int BC) {
   extern __shared__ float smem[];
   constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
   const int BCP = (BC + 15) & ~15, nkb = BCP / 16;
@@ -41,32 +41,33 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   float* vs = smem + BCP * LD;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int ntq = (n + BR - 1) / BR;
+  const int ntq = (nq + BR - 1) / BR;
   const int head = blockIdx.x % bh;
   const int q0 = (ntq - 1 - blockIdx.x / bh) * BR;
   const int q0w = q0 + 16 * wave;
   const int qr = q0w + l16;
-  const size_t hoff = (size_t)head * n * D;
+  const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
 
   // B operand of S^T = K Q^T: lane holds Q[qr][4st + g]
   float qf[NST];
 #pragma unroll
-  for (int st = 0; st < NST; ++st) qf[st] = (qr < n) ? Q[hoff + (size_t)qr * D + 4 * st + g] : 0.f;
+  for (int st = 0; st < NST; ++st) qf[st] = (qr < nq) ? Q[hoffq + (size_t)qr * D + 4 * st + g] : 0.f;
   f32x4 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
 
-  const int kend = CAUSAL ? min(n, q0 + BR) : n;
+  const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
   const int ntk = (kend + BC - 1) / BC;
   for (int j = 0; j < ntk; ++j) {
     const int j0 = j * BC;
-    const int valid = min(BC, n - j0);
+    const int valid = min(BC, nk - j0);
     __syncthreads();
-    stage_f32_rows<D>(ks, K + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
-    stage_f32_rows<D>(vs, V + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
+    stage_f32_rows<D>(ks, K + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
+    stage_f32_rows<D>(vs, V + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
     __syncthreads();
-    if (CAUSAL && j0 > q0w + 15) continue;
+    if (CAUSAL && j0 > q0w + 15 + off) continue;
     // S^T: lane holds key j0 + 16kb + 4g + i, query qr
     f32x4 s[kMaxBlk];
     float mx = kNegInf;
@@ -79,7 +80,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kl = 16 * kb + 4 * g + i;
-          if (kl >= valid || (CAUSAL && j0 + kl > qr)) c[i] = kNegInf;
+          if (kl >= valid || (CAUSAL && j0 + kl > qr + off)) c[i] = kNegInf;
           mx = fmaxf(mx, c[i]);
         }
         s[kb] = c;
@@ -119,14 +120,14 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     }
   }
   const float lt = wave_sum_xor16_32(lsum);
-  if (qr < n) {
+  if (qr < nq) {
     const float inv = 1.f / lt;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       f32x4 o4 = acc[db] * inv;
-      *reinterpret_cast<f32x4*>(O + hoff + (size_t)qr * D + 16 * db + 4 * g) = o4;
+      *reinterpret_cast<f32x4*>(O + hoffq + (size_t)qr * D + 16 * db + 4 * g) = o4;
     }
-    if (g == 0) LSE[(size_t)head * n + qr] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+    if (g == 0) LSE[(size_t)head * nq + qr] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
   }
 }
 
@@ -136,7 +137,7 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                      const float* __restrict__ V, const float* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ DELTA,
                      float* __restrict__ dK, float* __restrict__ dV,
-                     int bh, int n, float scale, float scale_log2, int BR, int BC) {
+                     int bh, int nq, int nk, float scale, float scale_log2, int BR, int BC) {
   extern __shared__ float smem[];
   constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
   float* qs = smem;
@@ -150,15 +151,16 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int k0 = (blockIdx.x / bh) * BC;
   const int k0w = k0 + 16 * wave;
   const int key = k0w + l16;
-  const bool key_ok = key < n && key < k0 + BC;
-  const size_t hoff = (size_t)head * n * D;
+  const bool key_ok = key < nk && key < k0 + BC;
+  const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
 
   // B operands of S = Q K^T and dP = dO V^T: lane holds K[key][4st + g], V[key][4st + g]
   float kf[NST], vf[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
-    kf[st] = key_ok ? K[hoff + (size_t)key * D + 4 * st + g] : 0.f;
-    vf[st] = key_ok ? V[hoff + (size_t)key * D + 4 * st + g] : 0.f;
+    kf[st] = key_ok ? K[hoffk + (size_t)key * D + 4 * st + g] : 0.f;
+    vf[st] = key_ok ? V[hoffk + (size_t)key * D + 4 * st + g] : 0.f;
   }
   f32x4 dk[NDB], dv[NDB];
 #pragma unroll
@@ -166,20 +168,20 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int ntq = (n + BR - 1) / BR;
-  const int it0 = CAUSAL ? k0 / BR : 0;
+  const int ntq = (nq + BR - 1) / BR;
+  const int it0 = CAUSAL ? max(0, k0 - off) / BR : 0;   // earlier queries see none of these keys
   for (int it = it0; it < ntq; ++it) {
     const int i0 = it * BR;
-    const int valid = min(BR, n - i0);
+    const int valid = min(BR, nq - i0);
     __syncthreads();
-    stage_f32_rows<D>(qs, Q + hoff + (size_t)i0 * D, BR, valid, tid, nthr);
-    stage_f32_rows<D>(os, dO + hoff + (size_t)i0 * D, BR, valid, tid, nthr);
+    stage_f32_rows<D>(qs, Q + hoffq + (size_t)i0 * D, BR, valid, tid, nthr);
+    stage_f32_rows<D>(os, dO + hoffq + (size_t)i0 * D, BR, valid, tid, nthr);
     for (int r = tid; r < BR; r += nthr) {
-      l2s[r] = (r < valid) ? LSE[(size_t)head * n + i0 + r] * kLog2e : __builtin_inff();
-      dsm[r] = (r < valid) ? DELTA[(size_t)head * n + i0 + r] : 0.f;
+      l2s[r] = (r < valid) ? LSE[(size_t)head * nq + i0 + r] * kLog2e : __builtin_inff();
+      dsm[r] = (r < valid) ? DELTA[(size_t)head * nq + i0 + r] : 0.f;
     }
     __syncthreads();
-    if (CAUSAL && i0 + BR - 1 < k0w) continue;
+    if (CAUSAL && i0 + BR - 1 + off < k0w) continue;
 #pragma unroll
     for (int qb = 0; qb < kMaxBlk; ++qb) {
       if (qb < nqb) {
@@ -196,7 +198,7 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int i = 0; i < 4; ++i) {
           const int rl = 16 * qb + 4 * g + i;
           float p = exp2_fast(__builtin_fmaf(s[i], scale_log2, -l2s[rl]));
-          if (CAUSAL && key > i0 + rl) p = 0.f;
+          if (CAUSAL && key > i0 + rl + off) p = 0.f;
           s[i] = p;
           dp[i] = p * (dp[i] - dsm[rl]);
         }
@@ -217,8 +219,8 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   if (key_ok) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      *reinterpret_cast<f32x4*>(dK + hoff + (size_t)key * D + 16 * db + 4 * g) = dk[db] * scale;
-      *reinterpret_cast<f32x4*>(dV + hoff + (size_t)key * D + 16 * db + 4 * g) = dv[db];
+      *reinterpret_cast<f32x4*>(dK + hoffk + (size_t)key * D + 16 * db + 4 * g) = dk[db] * scale;
+      *reinterpret_cast<f32x4*>(dV + hoffk + (size_t)key * D + 16 * db + 4 * g) = dv[db];
     }
   }
 }
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(512)
 void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                    const float* __restrict__ V, const float* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                   float* __restrict__ dQ, int bh, int n, float scale, float scale_log2,
+                   float* __restrict__ dQ, int bh, int nq, int nk, float scale, float scale_log2,
                    int BR, int BC) {
   extern __shared__ float smem[];
   constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
@@ -237,35 +239,36 @@ void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   float* vs = smem + BCP * LD;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int ntq = (n + BR - 1) / BR;
+  const int ntq = (nq + BR - 1) / BR;
   const int head = blockIdx.x % bh;
   const int q0 = (ntq - 1 - blockIdx.x / bh) * BR;
   const int q0w = q0 + 16 * wave;
   const int qr = q0w + l16;
-  const size_t hoff = (size_t)head * n * D;
+  const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
 
   float qf[NST], of[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
-    qf[st] = (qr < n) ? Q[hoff + (size_t)qr * D + 4 * st + g] : 0.f;
-    of[st] = (qr < n) ? dO[hoff + (size_t)qr * D + 4 * st + g] : 0.f;
+    qf[st] = (qr < nq) ? Q[hoffq + (size_t)qr * D + 4 * st + g] : 0.f;
+    of[st] = (qr < nq) ? dO[hoffq + (size_t)qr * D + 4 * st + g] : 0.f;
   }
-  const float l2q = (qr < n) ? LSE[(size_t)head * n + qr] * kLog2e : __builtin_inff();
-  const float dd = (qr < n) ? DELTA[(size_t)head * n + qr] : 0.f;
+  const float l2q = (qr < nq) ? LSE[(size_t)head * nq + qr] * kLog2e : __builtin_inff();
+  const float dd = (qr < nq) ? DELTA[(size_t)head * nq + qr] : 0.f;
   f32x4 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int kend = CAUSAL ? min(n, q0 + BR) : n;
+  const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
   const int ntk = (kend + BC - 1) / BC;
   for (int j = 0; j < ntk; ++j) {
     const int j0 = j * BC;
-    const int valid = min(BC, n - j0);
+    const int valid = min(BC, nk - j0);
     __syncthreads();
-    stage_f32_rows<D>(ks, K + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
-    stage_f32_rows<D>(vs, V + hoff + (size_t)j0 * D, BCP, valid, tid, nthr);
+    stage_f32_rows<D>(ks, K + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
+    stage_f32_rows<D>(vs, V + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
     __syncthreads();
-    if (CAUSAL && j0 > q0w + 15) continue;
+    if (CAUSAL && j0 > q0w + 15 + off) continue;
 #pragma unroll
     for (int kb = 0; kb < kMaxBlk; ++kb) {
       if (kb < nkb) {
@@ -282,7 +285,7 @@ void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int i = 0; i < 4; ++i) {
           const int kl = 16 * kb + 4 * g + i;
           float p = exp2_fast(__builtin_fmaf(s[i], scale_log2, -l2q));
-          if (kl >= valid || (CAUSAL && j0 + kl > qr)) p = 0.f;
+          if (kl >= valid || (CAUSAL && j0 + kl > qr + off)) p = 0.f;
           dp[i] = p * (dp[i] - dd);
         }
         // dQ^T += K^T dS^T: step t carries key 16kb + 4g + t
@@ -295,10 +298,10 @@ void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       }
     }
   }
-  if (qr < n) {
+  if (qr < nq) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4*>(dQ + hoff + (size_t)qr * D + 16 * db + 4 * g) = acc[db] * scale;
+      *reinterpret_cast<f32x4*>(dQ + hoffq + (size_t)qr * D + 16 * db + 4 * g) = acc[db] * scale;
   }
 }
 
@@ -325,17 +328,17 @@ static hipError_t set_lds(KernelT kern, size_t bytes) {
   }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int bh, int n, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                           hipStream_t st) {
   const size_t lds = f32_lds_bytes(0, d, bm, bn);
-  const dim3 grid((unsigned)(((n + bm - 1) / bm) * bh)), block(bm * 4);
+  const dim3 grid((unsigned)(((nq + bm - 1) / bm) * bh)), block(bm * 4);
   const float sl2 = scale * kLog2e;
 #define FA_FWD_F32(DD)                                                                      \
   {                                                                                         \
     auto kern = causal ? fwd_f32_kernel<DD, true> : fwd_f32_kernel<DD, false>;              \
     hipError_t e = set_lds(kern, lds);                                                      \
     if (e != hipSuccess) return e;                                                          \
-    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, o, lse, bh, n, sl2, bm, bn);    \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, o, lse, bh, nq, nk, sl2, bm, bn); \
   }
   FA_F32_DISPATCH_D(FA_FWD_F32)
 #undef FA_FWD_F32
@@ -344,17 +347,18 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 
 hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const float* dO,
                            const float* lse, const float* delta, float* dk, float* dv,
-                           int bh, int n, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                            hipStream_t st) {
   const size_t lds = f32_lds_bytes(1, d, bm, bn);
-  const dim3 grid((unsigned)(((n + bn - 1) / bn) * bh)), block(((bn + 15) / 16) * 64);
+  const dim3 grid((unsigned)(((nk + bn - 1) / bn) * bh)), block(((bn + 15) / 16) * 64);
   const float sl2 = scale * kLog2e;
 #define FA_DKDV_F32(DD)                                                                     \
   {                                                                                         \
     auto kern = causal ? dkdv_f32_kernel<DD, true> : dkdv_f32_kernel<DD, false>;            \
     hipError_t e = set_lds(kern, lds);                                                      \
     if (e != hipSuccess) return e;                                                          \
-    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dk, dv, bh, n,  \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dk, dv, bh, nq, \
+                       nk,                                                                  \
                        scale, sl2, bm, bn);                                                 \
   }
   FA_F32_DISPATCH_D(FA_DKDV_F32)
@@ -364,17 +368,17 @@ hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const
 
 hipError_t launch_dq_f32(const float* q, const float* k, const float* v, const float* dO,
                          const float* lse, const float* delta, float* dq,
-                         int bh, int n, int d, float scale, int causal, int bm, int bn,
+                         int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                          hipStream_t st) {
   const size_t lds = f32_lds_bytes(2, d, bm, bn);
-  const dim3 grid((unsigned)(((n + bm - 1) / bm) * bh)), block(bm * 4);
+  const dim3 grid((unsigned)(((nq + bm - 1) / bm) * bh)), block(bm * 4);
   const float sl2 = scale * kLog2e;
 #define FA_DQ_F32(DD)                                                                       \
   {                                                                                         \
     auto kern = causal ? dq_f32_kernel<DD, true> : dq_f32_kernel<DD, false>;                \
     hipError_t e = set_lds(kern, lds);                                                      \
     if (e != hipSuccess) return e;                                                          \
-    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dq, bh, n,      \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dq, bh, nq, nk,  \
                        scale, sl2, bm, bn);                                                 \
   }
   FA_F32_DISPATCH_D(FA_DQ_F32)
@@ -422,9 +426,9 @@ static hipError_t launch_pre_inst(const void* o, const void* dO, float* delta, l
   return hipGetLastError();
 }
 
-hipError_t launch_preprocess(const void* o, const void* dO, float* delta, int bh, int n, int d,
+hipError_t launch_preprocess(const void* o, const void* dO, float* delta, int bh, int nq, int d,
                              int dtype, hipStream_t st) {
-  const long long rows = (long long)bh * n;
+  const long long rows = (long long)bh * nq;
   if (dtype == 0) {
     switch (d) {
       case 16: return launch_pre_inst<float, 16>(o, dO, delta, rows, st);

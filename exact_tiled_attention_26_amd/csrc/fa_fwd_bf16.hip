@@ -40,12 +40,14 @@ namespace fa {
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kFwdBuffers = 2;   // LDS buffers per operand (copy distance NBUF - 1 tiles)
 
-// RAGGED: n may not be a multiple of BC (the last key tile needs the mask).
+// nq query rows attend to nk key rows; causal masking is aligned to the end
+// of the key sequence (query i sees keys 0 .. i + nk - nq).
+// RAGGED: nk may not be a multiple of BC (the last key tile needs the mask).
 template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED, int NBUF>
 __global__ __launch_bounds__(NW * 64, 2)
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                     float* __restrict__ LSE, int bh, int n, float scale_log2) {
+                     float* __restrict__ LSE, int bh, int nq, int nk, float scale_log2) {
   constexpr int BR = QW * NW;
   constexpr int NQB = QW / 16;   // 16-query blocks per wave
   constexpr int NKB = BC / 16;   // 16-key blocks per tile
@@ -67,26 +69,26 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int ntq = (n + BR - 1) / BR;
+  const int ntq = (nq + BR - 1) / BR;
   const int head = blockIdx.x % bh;
   const int qt = ntq - 1 - blockIdx.x / bh;
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
-  const size_t hoff = (size_t)head * n * D;
-  const __bf16* Qh = Q + hoff;
-  const __bf16* Kh = K + hoff;
-  const __bf16* Vh = V + hoff;
+  const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const __bf16* Qh = Q + (size_t)head * nq * D;
+  const __bf16* Kh = K + (size_t)head * nk * D;
+  const __bf16* Vh = V + (size_t)head * nk * D;
 
-  const int kend = CAUSAL ? min(n, q0 + BR) : n;   // keys this workgroup can see
+  const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;   // keys this workgroup can see
   const int ntk = (kend + BC - 1) / BC;
   // last key tile with a key that one of this wave's rows can see
   // (dz: see divergent_zero)
   const int dz = divergent_zero();
-  const int last = CAUSAL ? min(ntk - 1, (q0w + QW - 1) / BC) : ntk - 1 + dz;
+  const int last = CAUSAL ? min(ntk - 1, (q0w + QW - 1 + off) / BC) : ntk - 1 + dz;
   const AsyncTileCopy<D, BC, NW> copier(wave, lane);
-  copier.issue(k_lds[0], Kh, min(BC, n));
-  if (ntk > 1) copier.issue(k_lds[1], Kh + (size_t)BC * D, n - BC);
-  copier.issue(v_lds[0], Vh, min(BC, n));
+  copier.issue(k_lds[0], Kh, min(BC, nk));
+  if (ntk > 1) copier.issue(k_lds[1], Kh + (size_t)BC * D, nk - BC);
+  copier.issue(v_lds[0], Vh, min(BC, nk));
 
   // Q rows of this wave as B operands: lane holds Q[q0w + 16qb + l16][32ds + 8g .. +7]
   bf16x8 qf[NQB][NDS];
@@ -95,7 +97,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int row = q0w + 16 * qb + l16;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      if (row < n) {
+      if (row < nq) {
         qf[qb][ds] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * D + 32 * ds + 8 * g);
       } else {
         qf[qb][ds] = bf16x8{};
@@ -125,11 +127,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // does key tile j need the in-tile mask for this wave?
   auto tile_masked = [&](int j) __attribute__((always_inline)) {
-    return (CAUSAL && j * BC + BC - 1 > q0w) || (RAGGED && j * BC + BC > n + dz);
+    return (CAUSAL && j * BC + BC - 1 > q0w + off) || (RAGGED && j * BC + BC > nk + dz);
   };
   // in-tile mask: key j0 + 16kb + 4g + i is visible iff 16kb + i <= lim
   auto mask_item = [&](f32x4 (&s)[NKB][NQB], int j0, int qb, int kb) __attribute__((always_inline)) {
-    const int lastq = CAUSAL ? min(q0w + 16 * qb + l16, n - 1) : n - 1;
+    const int lastq = CAUSAL ? min(q0w + 16 * qb + l16 + off, nk - 1) : nk - 1;
     const int lim = lastq - j0 - 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -184,8 +186,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   async_copy_wait();
   // copies that step 0 waits for when the distance is two steps
   if constexpr (NBUF == 3) {
-    if (ntk > 1) copier.issue(v_lds[1], Vh + (size_t)BC * D, n - BC);
-    if (ntk > 2) copier.issue(k_lds[2], Kh + (size_t)2 * BC * D, n - 2 * BC);
+    if (ntk > 1) copier.issue(v_lds[1], Vh + (size_t)BC * D, nk - BC);
+    if (ntk > 2) copier.issue(k_lds[2], Kh + (size_t)2 * BC * D, nk - 2 * BC);
   }
   __syncthreads();
   s_gemm_plain(sa, k_lds[0]);
@@ -310,8 +312,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto step = [&](f32x4 (&sc)[NKB][NQB], f32x4 (&sn)[NKB][NQB], int t) __attribute__((always_inline)) {
     const int b0 = t % NBUF, b1 = (t + 1) % NBUF, bl = (t + NBUF - 1) % NBUF;
     const bool ck = t + NBUF < ntk, cv = t + NBUF - 1 < ntk;
-    if (cv) copier.issue(v_lds[bl], Vh + (size_t)(t + NBUF - 1) * BC * D, n - (t + NBUF - 1) * BC);
-    if (ck) copier.issue(k_lds[b0], Kh + (size_t)(t + NBUF) * BC * D, n - (t + NBUF) * BC);
+    if (cv) copier.issue(v_lds[bl], Vh + (size_t)(t + NBUF - 1) * BC * D, nk - (t + NBUF - 1) * BC);
+    if (ck) copier.issue(k_lds[b0], Kh + (size_t)(t + NBUF) * BC * D, nk - (t + NBUF) * BC);
     if (t <= last) {
       const __bf16* kn = k_lds[b1];
       const __bf16* vt = v_lds[b0];
@@ -347,8 +349,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const float lt = wave_sum_xor16_32(lsum[qb]);
     const float inv = 1.f / lt;
     const int qr = q0w + 16 * qb + l16;
-    if (qr < n) {
-      __bf16* orow = O + hoff + (size_t)qr * D;
+    if (qr < nq) {
+      __bf16* orow = O + (size_t)head * nq * D + (size_t)qr * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         bf16x4 o4;
@@ -356,34 +358,34 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(acc[db][qb][i] * inv);
         *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g) = o4;
       }
-      if (g == 0) LSE[(size_t)head * n + qr] = (m[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
+      if (g == 0) LSE[(size_t)head * nq + qr] = (m[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
     }
   }
 }
 
 template <int D, int QW, int NW, int BC>
 static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, void* o, float* lse,
-                                  int bh, int n, float scale, int causal, hipStream_t st) {
+                                  int bh, int nq, int nk, float scale, int causal, hipStream_t st) {
   constexpr int BR = QW * NW;
-  const int ntq = (n + BR - 1) / BR;
+  const int ntq = (nq + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
   auto kern = causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true, kFwdBuffers>
-            : (n % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, kFwdBuffers>
+            : (nk % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, kFwdBuffers>
                        : fwd_bf16_kernel<D, QW, NW, BC, false, false, kFwdBuffers>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (__bf16*)o, lse, bh, n, sl2);
+                     (__bf16*)o, lse, bh, nq, nk, sl2);
   return hipGetLastError();
 }
 
 // Tuned tilings: (head dim, BR, BC) -> instance.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int bh, int n, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                            hipStream_t st) {
-  if (d == 128 && bm == 128 && bn == 64) return launch_fwd_inst<128, 32, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
-  if (d == 128 && bm == 256 && bn == 64) return launch_fwd_inst<128, 32, 8, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
-  if (d == 64 && bm == 128 && bn == 64) return launch_fwd_inst<64, 32, 4, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
-  if (d == 64 && bm == 256 && bn == 64) return launch_fwd_inst<64, 32, 8, 64>(q, k, v, o, lse, bh, n, scale, causal, st);
+  if (d == 128 && bm == 128 && bn == 64) return launch_fwd_inst<128, 32, 4, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
+  if (d == 128 && bm == 256 && bn == 64) return launch_fwd_inst<128, 32, 8, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
+  if (d == 64 && bm == 128 && bn == 64) return launch_fwd_inst<64, 32, 4, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
+  if (d == 64 && bm == 256 && bn == 64) return launch_fwd_inst<64, 32, 8, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
   return hipErrorInvalidValue;
 }
 

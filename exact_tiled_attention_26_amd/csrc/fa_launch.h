@@ -1,6 +1,11 @@
 // Host-side launchers behind the C ABI (include/fa.h).  Each returns the
 // HIP error of its launch; arguments were validated by the caller.  A tiling
 // that has no kernel instance returns hipErrorInvalidValue.
+//
+// nq query rows (Q, O, dO, dQ, L, D) attend to nk key rows (K, V, dK, dV).
+// Causal masking is aligned to the end of the key sequence: query i sees key
+// j iff j <= i + (nk - nq); the caller guarantees nk >= nq when causal and
+// nq, nk >= 1.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,31 +13,31 @@
 namespace fa {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int bh, int n, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                            hipStream_t st);
 hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO,
                             const float* lse, const float* delta, void* dk, void* dv,
-                            int bh, int n, int d, float scale, int causal, int bm, int bn,
+                            int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                             hipStream_t st);
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO,
                           const float* lse, const float* delta, void* dq,
-                          int bh, int n, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                           hipStream_t st);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int bh, int n, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                           hipStream_t st);
 hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const float* dO,
                            const float* lse, const float* delta, float* dk, float* dv,
-                           int bh, int n, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                            hipStream_t st);
 hipError_t launch_dq_f32(const float* q, const float* k, const float* v, const float* dO,
                          const float* lse, const float* delta, float* dq,
-                         int bh, int n, int d, float scale, int causal, int bm, int bn,
+                         int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
                          hipStream_t st);
 
 // dtype: 0 = float32, 1 = bf16
-hipError_t launch_preprocess(const void* o, const void* dO, float* delta, int bh, int n, int d,
+hipError_t launch_preprocess(const void* o, const void* dO, float* delta, int bh, int nq, int d,
                              int dtype, hipStream_t st);
 
 // LDS bytes the float32 kernels need for a tiling (host-side check).

@@ -12,6 +12,11 @@
  *   fa_bwd_dkdv        dK, dV: outer loop over key/value tiles, P recomputed
  *                      on chip as exp(S - L).
  *   fa_bwd_dq          dQ: outer loop over query tiles, P recomputed again.
+ *   fa_fwd_rect, fa_bwd_dkdv_rect, fa_bwd_dq_rect
+ *                      the same with nq queries attending to nk keys
+ *                      (causal masking aligned to the end of the keys), for
+ *                      a chunk of new queries against a longer key/value
+ *                      cache; fa_bwd_preprocess serves both forms.
  *
  * Source of the method (cited by page and section):
  *   "Assignment2: FlashAttention & Distributed Data Parallel notes"
@@ -22,7 +27,8 @@
  *   two-kernel backward that needs no atomics).
  *   "CS349E lecture 11, 03_flash_backward.py" demo1_gradcheck (D from one row
  *   of O and dO, computed before the backward), demo4_causal (only tiles
- *   crossing the diagonal need an in-tile mask).
+ *   crossing the diagonal need an in-tile mask; in decode one new token
+ *   sees every cached key).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -57,6 +63,14 @@
  *   independent of each other).
  * Empty input.  bh == 0 or n == 0 is a no-op that returns FA_OK (pointers
  *   are not touched and may be NULL).
+ * Queries and keys of different lengths (the *_rect calls).  q, o, dO, dq
+ *   are [bh][nq][d], lse and delta [bh][nq]; k, v, dk, dv are [bh][nk][d].
+ *   With causal != 0 the queries are the last nq positions of the key
+ *   sequence: key j is visible to query i iff j <= i + (nk - nq), so every
+ *   row sees at least one key; causal with nq > nk would leave rows with no
+ *   key and returns FA_ERR_UNSUPPORTED.  bh == 0 or nq == nk == 0 is a
+ *   no-op; exactly one of nq, nk zero is FA_ERR_INVALID_ARG.  The square
+ *   calls are the case nq = nk = n.
  * Errors.  Arguments are validated on the host before any HIP call; an
  *   invalid call launches nothing and returns a non-zero status.  A launch
  *   failure reported by the HIP runtime returns FA_ERR_HIP.  Faults during
@@ -70,7 +84,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
@@ -107,6 +121,21 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                     const float* lse, const float* delta, void* dq,
                     int bh, int n, int d, fa_dtype dtype, float scale, int causal,
                     int block_m, int block_n, void* stream);
+
+/* The three calls above for nq queries against nk keys (see "Queries and
+ * keys of different lengths").  fa_bwd_preprocess(o, dO, delta, bh, nq, d,
+ * ...) provides delta. */
+fa_status fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int bh, int nq, int nk, int d, fa_dtype dtype, float scale, int causal,
+                      int block_m, int block_n, void* stream);
+fa_status fa_bwd_dkdv_rect(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lse, const float* delta, void* dk, void* dv,
+                           int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
+                           int causal, int block_m, int block_n, void* stream);
+fa_status fa_bwd_dq_rect(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* delta, void* dq,
+                         int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
+                         int causal, int block_m, int block_n, void* stream);
 
 /* The tiling (block_m, block_n) that block_m = block_n = 0 selects for a
  * kernel (0 = fwd, 1 = dkdv, 2 = dq) at this dtype and head dim.  Returns

@@ -9,7 +9,11 @@ the full score matrix of each head, in fp64:
 
 1. ``S = scale * Q K^T``                       ([CS336-A2] 1.1; 1.4 Eq 13)
 2. causal: ``S_ij = -inf`` for key ``j > i``    ([CS324-L8] demo4_backward,
-   lower-triangular ``tril`` mask; query ``i`` sees keys ``0..i``)
+   lower-triangular ``tril`` mask; query ``i`` sees keys ``0..i``).  With
+   ``N_q`` queries against ``N_k >= N_q`` keys the queries are the last
+   ``N_q`` positions: key ``j`` is masked iff ``j > i + (N_k - N_q)`` (the
+   decode remark of [CS349E-L11] demo4_causal: one new query sees every
+   cached key); ``N_q = N_k`` is the square case.
 3. ``m_i = max_j S_ij``, ``L_i = m_i + ln sum_j exp(S_ij - m_i)``
    (the logsumexp saved by the forward, [CS336-A2] 1.2)
 4. ``P = exp(S - L)``                          ([CS336-A2] 1.4 Eq 14)
@@ -45,15 +49,25 @@ def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def _causal_offset(nq: int, nk: int, causal: bool) -> int:
+    """Shift of the causal diagonal: query i sees keys 0 .. i + (nk - nq)."""
+    if not causal:
+        return 0
+    if nq > nk:
+        raise ValueError(f"causal attention needs at least as many keys as queries (nq={nq}, nk={nk})")
+    return nk - nq
+
+
 def _scores(q_rows: np.ndarray, k: np.ndarray, scale: float, causal: bool,
-            row_idx: np.ndarray, col_idx: np.ndarray | None = None) -> np.ndarray:
+            row_idx: np.ndarray, col_idx: np.ndarray | None = None, offset: int = 0) -> np.ndarray:
     """Steps 1-2: scaled scores of the given query rows against keys ``col_idx``
-    (all keys when None), with the causal mask applied by global index."""
+    (all keys when None), with the causal mask applied by global index
+    (key j visible to query i iff j <= i + offset)."""
     if col_idx is None:
         col_idx = np.arange(k.shape[0])
     s = scale * (q_rows @ k.T)
     if causal:
-        s = np.where(col_idx[None, :] > row_idx[:, None], -np.inf, s)
+        s = np.where(col_idx[None, :] > row_idx[:, None] + offset, -np.inf, s)
     return s
 
 
@@ -67,11 +81,12 @@ def _logsumexp_rows(s: np.ndarray) -> np.ndarray:
 
 def _forward_head(q, k, v, scale, causal, chunk):
     n = q.shape[0]
+    off = _causal_offset(n, k.shape[0], causal)
     o = np.empty((n, v.shape[1]))
     lse = np.empty(n)
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k, scale, causal, rows)
+        s = _scores(q[rows], k, scale, causal, rows, offset=off)
         lse[rows] = _logsumexp_rows(s)
         p = np.exp(s - lse[rows][:, None])            # step 4
         o[rows] = p @ v                                 # step 5
@@ -80,13 +95,14 @@ def _forward_head(q, k, v, scale, causal, chunk):
 
 def _backward_head(q, k, v, do, scale, causal, chunk):
     n = q.shape[0]
+    off = _causal_offset(n, k.shape[0], causal)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     delta = np.empty(n)
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k, scale, causal, rows)
+        s = _scores(q[rows], k, scale, causal, rows, offset=off)
         lse = _logsumexp_rows(s)
         p = np.exp(s - lse[:, None])                    # step 4
         dv += p.T @ do[rows]                            # step 6
@@ -108,7 +124,8 @@ def _batched(fn, arrays, *args):
 
 
 def attention_forward(q, k, v, scale=None, causal=False, chunk=DEFAULT_CHUNK):
-    """Return ``(O, L)`` for q, k, v of shape [N, d] or [BH, N, d] (fp64)."""
+    """Return ``(O, L)`` for q of shape [N_q, d] or [BH, N_q, d] and k, v of
+    shape [N_k, d] or [BH, N_k, d] (fp64)."""
     scale = _default_scale(np.shape(q)[-1], scale)
     return _batched(_forward_head, (q, k, v), scale, bool(causal), int(chunk))
 
@@ -141,7 +158,7 @@ def forward_rows(q, k, v, rows, scale=None, causal=False):
     q, k, v = _f64(q), _f64(k), _f64(v)
     scale = _default_scale(q.shape[1], scale)
     rows = np.asarray(rows, dtype=np.int64)
-    s = _scores(q[rows], k, scale, causal, rows)
+    s = _scores(q[rows], k, scale, causal, rows, offset=_causal_offset(q.shape[0], k.shape[0], causal))
     lse = _logsumexp_rows(s)
     return np.exp(s - lse[:, None]) @ v, lse
 
@@ -152,7 +169,7 @@ def dq_rows(q, k, v, do, rows, scale=None, causal=False):
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     scale = _default_scale(q.shape[1], scale)
     rows = np.asarray(rows, dtype=np.int64)
-    s = _scores(q[rows], k, scale, causal, rows)
+    s = _scores(q[rows], k, scale, causal, rows, offset=_causal_offset(q.shape[0], k.shape[0], causal))
     p = np.exp(s - _logsumexp_rows(s)[:, None])
     dp = do[rows] @ v.T
     delta = (p * dp).sum(axis=1)
@@ -165,11 +182,12 @@ def head_row_stats(q, k, v, do, scale=None, causal=False, chunk=DEFAULT_CHUNK):
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     scale = _default_scale(q.shape[1], scale)
     n = q.shape[0]
+    off = _causal_offset(n, k.shape[0], causal)
     lse = np.empty(n)
     delta = np.empty(n)
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k, scale, causal, rows)
+        s = _scores(q[rows], k, scale, causal, rows, offset=off)
         lse[rows] = _logsumexp_rows(s)
         p = np.exp(s - lse[rows][:, None])
         delta[rows] = (p * (do[rows] @ v.T)).sum(axis=1)
@@ -189,11 +207,12 @@ def dkdv_cols(q, k, v, do, cols, scale=None, causal=False, stats=None,
         stats = head_row_stats(q, k, v, do, scale, causal, chunk)
     lse, delta = stats
     n = q.shape[0]
+    off = _causal_offset(n, k.shape[0], causal)
     dk = np.zeros((len(cols), k.shape[1]))
     dv = np.zeros((len(cols), v.shape[1]))
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k[cols], scale, causal, rows, cols)
+        s = _scores(q[rows], k[cols], scale, causal, rows, cols, offset=off)
         p = np.exp(s - lse[rows][:, None])
         dv += p.T @ do[rows]
         dp = do[rows] @ v[cols].T

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     for code in range(5):
         assert fa.fa_status_str(code)
     assert fa.fa_status_str(99) == "unknown status"
@@ -145,6 +145,37 @@ def test_tilings(lib):
         assert dq(lib, bm=bm, bn=bn, dtype=fa.FA_F32, d=32, q=0) == fa.FA_ERR_INVALID_ARG
 
 
+def rect(lib, fn, **kw):
+    a = dict(q=A, k=B, v=C, dO=D_, lse=E, delta=F, o=D_, dq=G, dk=G, dv=H, bh=1, nq=64, nk=128, d=64,
+             dtype=fa.FA_BF16, scale=0.125, causal=1, bm=0, bn=0)
+    a.update(kw)
+    if fn == "fwd":
+        return lib.fa_fwd_rect(a["q"], a["k"], a["v"], a["o"], a["lse"], a["bh"], a["nq"], a["nk"], a["d"],
+                               a["dtype"], a["scale"], a["causal"], a["bm"], a["bn"], None)
+    if fn == "dkdv":
+        return lib.fa_bwd_dkdv_rect(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dk"], a["dv"],
+                                    a["bh"], a["nq"], a["nk"], a["d"], a["dtype"], a["scale"], a["causal"],
+                                    a["bm"], a["bn"], None)
+    return lib.fa_bwd_dq_rect(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dq"], a["bh"],
+                              a["nq"], a["nk"], a["d"], a["dtype"], a["scale"], a["causal"], a["bm"], a["bn"],
+                              None)
+
+
+def test_rect_lengths(lib):
+    for fn in ("fwd", "dkdv", "dq"):
+        # causal needs every query to see a key: nq <= nk
+        assert rect(lib, fn, nq=129, nk=128) == fa.FA_ERR_UNSUPPORTED
+        assert rect(lib, fn, nq=129, nk=128, causal=0, q=0) == fa.FA_ERR_INVALID_ARG   # accepted, then null q
+        # exactly one empty length has no meaning; both empty (or bh = 0) is a no-op
+        assert rect(lib, fn, nq=0, nk=5) == fa.FA_ERR_INVALID_ARG
+        assert rect(lib, fn, nq=5, nk=0, causal=0) == fa.FA_ERR_INVALID_ARG
+        assert rect(lib, fn, nq=0, nk=0, q=0, k=0) == fa.FA_OK
+        assert rect(lib, fn, bh=0, q=0, k=0) == fa.FA_OK
+        assert rect(lib, fn, nq=-1) == fa.FA_ERR_INVALID_ARG
+        assert rect(lib, fn, nk=(1 << 24) + 1, causal=0) == fa.FA_ERR_UNSUPPORTED
+        assert rect(lib, fn, q=A + 2) == fa.FA_ERR_MISALIGNED
+
+
 def test_empty_input_is_noop(lib):
     # bh == 0 or n == 0: nothing to do, pointers are not touched
     assert fwd(lib, q=0, k=0, v=0, o=0, lse=0, bh=0) == fa.FA_OK
@@ -176,6 +207,8 @@ def test_autograd_op_validates_on_host():
     with pytest.raises(ValueError):
         fa.flash_attention(q, q, q)                      # host tensors are refused
     with pytest.raises(ValueError):
-        fa.flash_attention(q, q[:, :8], q[:, :8])        # shapes must agree
+        fa.flash_attention(q, q[:, :, :32], q[:, :, :32])  # head dims must agree
+    with pytest.raises(ValueError):
+        fa.flash_attention(q, q[:1], q[:1])              # leading dims must agree
     with pytest.raises(ValueError):
         fa.flash_attention(q[0, 0], q[0, 0], q[0, 0])    # needs [..., n, d]

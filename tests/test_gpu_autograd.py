@@ -27,10 +27,12 @@ def _say(msg):
 
 
 def reference_attention(q, k, v, causal, scale):
+    """Causal masks are aligned to the end of the keys: query i sees keys
+    0 .. i + nk - nq."""
     s = scale * torch.matmul(q, k.transpose(-1, -2))
     if causal:
-        n = q.shape[-2]
-        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+        nq, nk = q.shape[-2], k.shape[-2]
+        s = s.masked_fill(torch.ones(nq, nk, dtype=torch.bool).triu(nk - nq + 1), float("-inf"))
     return torch.matmul(torch.softmax(s, dim=-1), v)
 
 
@@ -39,13 +41,17 @@ def _rel(err, ref):
     return err / (m if m > 0 else 1.0)
 
 
-@pytest.mark.parametrize("dtype,shape", [(torch.float32, (2, 3, 77, 32)),
-                                         (torch.bfloat16, (2, 2, 300, 64))])
+@pytest.mark.parametrize("dtype,shape,nk", [(torch.float32, (2, 3, 77, 32), 77),
+                                            (torch.bfloat16, (2, 2, 300, 64), 300),
+                                            (torch.float32, (2, 2, 50, 32), 130),
+                                            (torch.bfloat16, (1, 3, 200, 128), 1000)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_matches_cpu_autograd(dtype, shape, causal):
-    _say(f"autograd dtype={dtype} shape={shape} causal={causal}")
+def test_matches_cpu_autograd(dtype, shape, nk, causal):
+    _say(f"autograd dtype={dtype} q={shape} nk={nk} causal={causal}")
     g = torch.Generator().manual_seed(7)
-    q, k, v, w = (torch.randn(shape, generator=g, dtype=torch.float64) for _ in range(4))
+    kshape = shape[:-2] + (nk, shape[-1])
+    q, w = (torch.randn(shape, generator=g, dtype=torch.float64) for _ in range(2))
+    k, v = (torch.randn(kshape, generator=g, dtype=torch.float64) for _ in range(2))
     qd, kd, vd = (t.to(dtype).cuda().requires_grad_(True) for t in (q, k, v))
     wd = w.to(dtype).cuda()
     out = fa.flash_attention(qd, kd, vd, causal=causal)
@@ -57,7 +63,7 @@ def test_matches_cpu_autograd(dtype, shape, causal):
     (ref * wd.cpu().double()).sum().backward()
 
     tol_o, tol_g = TOL[dtype]
-    assert out.shape == ref.shape and out.dtype == dtype
+    assert out.shape == ref.shape == q.shape and out.dtype == dtype
     err_o = (out.detach().cpu().double() - ref.detach()).abs().max().item()
     assert err_o <= tol_o, err_o
     for name, a, b in (("dq", qd.grad, qc.grad), ("dk", kd.grad, kc.grad), ("dv", vd.grad, vc.grad)):

@@ -18,7 +18,7 @@ import torch
 
 import exact_tiled_attention_26_amd as fa
 import oracle
-from workloads import WORKLOADS, cast_io, make_inputs, to_f64
+from workloads import WORKLOADS, cast_io, make_inputs, make_rect_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -249,3 +249,46 @@ def test_long_context_sampled_and_memory():
     nxn_bytes = w.bh * w.n * w.n * 2
     _say(f"peak {peak / 2**20:.1f} MiB, I/O {io_bytes / 2**20:.1f} MiB, one bf16 P would be {nxn_bytes / 2**30:.1f} GiB")
     assert peak <= io_bytes * 1.05 + (8 << 20)
+
+
+# --------------------------------------------------------------------------- nq != nk
+# nq queries against nk keys through the *_rect calls (the binding picks them
+# when k is longer or shorter than q); causal masks are aligned to the end of
+# the keys.  Sizes span several tiles with ragged ends on both axes.
+@pytest.mark.parametrize("nq,nk", [(37, 100), (1, 64), (64, 200), (200, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rect_fp32(nq, nk, causal):
+    if causal and nq > nk:
+        pytest.skip("causal needs nq <= nk")
+    arrays = make_rect_inputs(2, nq, nk, 32, seed=30)
+    for tiles in ((16, 12), (64, 64)):
+        g = run_gpu(arrays, "fp32", causal, tiles, tiles, tiles)
+        compare_full(g, "fp32", causal, label=f"fp32 rect {nq}x{nk} tiles={tiles} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nq,nk", [(300, 1000), (1, 513), (256, 4096), (500, 200)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rect_bf16(d, nq, nk, causal):
+    if causal and nq > nk:
+        pytest.skip("causal needs nq <= nk")
+    arrays = make_rect_inputs(2, nq, nk, d, seed=31)
+    g = run_gpu(arrays, "bf16", causal)
+    compare_full(g, "bf16", causal, label=f"bf16 rect d={d} {nq}x{nk} causal={causal}")
+
+
+def test_rect_decode_matches_noncausal():
+    """One new query sees every cached key: causal and non-causal agree."""
+    arrays = make_rect_inputs(4, 1, 700, 128, seed=32)
+    a = run_gpu(arrays, "bf16", True)
+    b = run_gpu(arrays, "bf16", False)
+    compare_full(a, "bf16", True, label="bf16 decode 1x700 causal")
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        scale = max(1.0, np.abs(b[name]).max())
+        assert np.abs(a[name] - b[name]).max() <= 1e-2 * scale, name
+
+
+def test_rect_rejects_causal_with_more_queries():
+    arrays = make_rect_inputs(1, 65, 64, 64, seed=33)
+    with pytest.raises(fa.FAError):
+        run_gpu(arrays, "bf16", True)

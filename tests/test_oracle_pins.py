@@ -387,3 +387,115 @@ def test_pins_catch_planted_mistakes():
     # a mask in the wrong direction changes the forward
     o_up, _ = oracle.attention_forward(q[::-1], k[::-1], v[::-1], causal=True)
     assert np.abs(o_up[::-1] - ro).max() > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Queries and keys of different lengths (causal mask aligned to the end of
+# the keys: query i sees keys 0 .. i + N_k - N_q)
+# --------------------------------------------------------------------------
+
+def _torch_rect_reference(q, k, v, do, causal, scale):
+    """torch SDPA on the CPU in float64 with an explicit boolean mask (True =
+    the key takes part) built from the end-aligned rule."""
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    nq, nk = q.shape[0], k.shape[0]
+    mask = None
+    if causal:
+        i = torch.arange(nq)[:, None]
+        j = torch.arange(nk)[None, :]
+        mask = j <= i + (nk - nq)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq[None, None], tk[None, None], tv[None, None], attn_mask=mask, scale=scale)[0, 0]
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    return out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(37, 100), (1, 64), (64, 64), (90, 31)])
+def test_rect_matches_torch_sdpa_mask(causal, nq, nk):
+    if causal and nq > nk:
+        pytest.skip("causal needs nq <= nk")
+    rng = np.random.default_rng(21)
+    d = 8
+    q, do = (rng.standard_normal((nq, d)) for _ in range(2))
+    k, v = (rng.standard_normal((nk, d)) for _ in range(2))
+    scale = 1 / math.sqrt(d)
+    o, lse = oracle.attention_forward(q, k, v, causal=causal, chunk=16)
+    dq, dk, dv, delta = oracle.attention_backward(q, k, v, do, causal=causal, chunk=16)
+    ro, rdq, rdk, rdv = _torch_rect_reference(q, k, v, do, causal, scale)
+    for a, b in ((o, ro), (dq, rdq), (dk, rdk), (dv, rdv)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * max(1.0, np.abs(b).max()))
+    np.testing.assert_allclose(delta, oracle.delta_from_output(o, do), atol=1e-12)
+
+
+def test_rect_causal_is_the_tail_of_square_attention():
+    """N_q queries against N_k keys, causal, equal the last N_q rows of square
+    causal attention over N_k queries whose last N_q rows are those queries;
+    with dO zero on the other rows, dK and dV are the square ones as well."""
+    rng = np.random.default_rng(22)
+    nk, nq, d = 120, 45, 16
+    q_full, k, v, do_full = (rng.standard_normal((nk, d)) for _ in range(4))
+    do_full[: nk - nq] = 0.0
+    o_sq, l_sq = oracle.attention_forward(q_full, k, v, causal=True)
+    dq_sq, dk_sq, dv_sq, _ = oracle.attention_backward(q_full, k, v, do_full, causal=True)
+    q, do = q_full[nk - nq:], do_full[nk - nq:]
+    o, lse = oracle.attention_forward(q, k, v, causal=True)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal=True)
+    np.testing.assert_allclose(o, o_sq[nk - nq:], atol=1e-14)
+    np.testing.assert_allclose(lse, l_sq[nk - nq:], atol=1e-13)
+    np.testing.assert_allclose(dq, dq_sq[nk - nq:], atol=1e-13)
+    np.testing.assert_allclose(dk, dk_sq, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_sq, atol=1e-13)
+
+
+def test_rect_decode_sees_every_key():
+    """One new query (decode) sees every cached key ([CS349E-L11]
+    demo4_causal observations), so causal and non-causal agree."""
+    rng = np.random.default_rng(23)
+    q, do = (rng.standard_normal((1, 32)) for _ in range(2))
+    k, v = (rng.standard_normal((200, 32)) for _ in range(2))
+    a = oracle.attention_forward(q, k, v, causal=True)
+    b = oracle.attention_forward(q, k, v, causal=False)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-15)
+    ga = oracle.attention_backward(q, k, v, do, causal=True)
+    gb = oracle.attention_backward(q, k, v, do, causal=False)
+    for x, y in zip(ga, gb):
+        np.testing.assert_allclose(x, y, atol=1e-15)
+
+
+def test_rect_causal_needs_enough_keys():
+    rng = np.random.default_rng(24)
+    q = rng.standard_normal((10, 4))
+    k = rng.standard_normal((9, 4))
+    with pytest.raises(ValueError):
+        oracle.attention_forward(q, k, k, causal=True)
+    rows = oracle.attention_forward(q, k, k, causal=False)[0]
+    assert rows.shape == (10, 4)
+
+
+def test_rect_sampled_outputs_match_full():
+    q, do = (a[0] for a in make_inputs(1, 70, 16, seed=25)[:2])
+    k, v = (a[0] for a in make_inputs(1, 150, 16, seed=26)[:2])
+    o, lse = oracle.attention_forward(q, k, v, causal=True)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal=True)
+    rows, cols = np.array([0, 33, 69]), np.array([0, 80, 149])
+    ro, rl = oracle.forward_rows(q, k, v, rows, causal=True)
+    np.testing.assert_allclose(ro, o[rows], atol=1e-14)
+    np.testing.assert_allclose(oracle.dq_rows(q, k, v, do, rows, causal=True)[0], dq[rows], atol=1e-13)
+    ck, cv = oracle.dkdv_cols(q, k, v, do, cols, causal=True)
+    np.testing.assert_allclose(ck, dk[cols], atol=1e-13)
+    np.testing.assert_allclose(cv, dv[cols], atol=1e-13)
+
+
+def test_rect_pins_catch_a_top_left_mask(monkeypatch):
+    """Aligning the rectangular causal mask to the start of the keys (offset
+    0) instead of their end is a plausible mistake; the torch reference with
+    the explicit end-aligned mask rejects it."""
+    rng = np.random.default_rng(27)
+    nq, nk, d = 20, 50, 8
+    q, do = (rng.standard_normal((nq, d)) for _ in range(2))
+    k, v = (rng.standard_normal((nk, d)) for _ in range(2))
+    ro = _torch_rect_reference(q, k, v, do, True, 1 / math.sqrt(d))[0]
+    monkeypatch.setattr(A, "_causal_offset", lambda nq_, nk_, causal: 0)
+    bad, _ = oracle.attention_forward(q, k, v, causal=True)
+    assert np.abs(bad - ro).max() > 1e-2

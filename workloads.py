@@ -67,6 +67,13 @@ def make_inputs(bh: int, n: int, d: int, seed: int = 0):
     return tuple(rng.standard_normal((bh, n, d)) for _ in range(4))
 
 
+def make_rect_inputs(bh: int, nq: int, nk: int, d: int, seed: int = 0):
+    """Like make_inputs for nq queries against nk keys: fp64 arrays drawn in
+    the order q [bh, nq, d], k [bh, nk, d], v [bh, nk, d], do [bh, nq, d]."""
+    rng = np.random.default_rng(seed)
+    return tuple(rng.standard_normal((bh, rows, d)) for rows in (nq, nk, nk, nq))
+
+
 def torch_dtype(name: str):
     import torch
     return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
