@@ -13,7 +13,9 @@ the full score matrix of each head, in fp64:
    ``N_q`` queries against ``N_k >= N_q`` keys the queries are the last
    ``N_q`` positions: key ``j`` is masked iff ``j > i + (N_k - N_q)`` (the
    decode remark of [CS349E-L11] demo4_causal: one new query sees every
-   cached key); ``N_q = N_k`` is the square case.
+   cached key); ``N_q = N_k`` is the square case.  A sliding window of
+   ``w`` keys ([CS324-L8] window_attention_torch: a row sees itself and the
+   ``w - 1`` keys before it) additionally masks ``j <= i + (N_k - N_q) - w``.
 3. ``m_i = max_j S_ij``, ``L_i = m_i + ln sum_j exp(S_ij - m_i)``
    (the logsumexp saved by the forward, [CS336-A2] 1.2)
 4. ``P = exp(S - L)``                          ([CS336-A2] 1.4 Eq 14)
@@ -49,6 +51,13 @@ def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def _check_window(causal: bool, window: int) -> int:
+    window = int(window)
+    if window < 0 or (window and not causal):
+        raise ValueError(f"a sliding window needs causal masking and window >= 1 (got {window})")
+    return window
+
+
 def _causal_offset(nq: int, nk: int, causal: bool) -> int:
     """Shift of the causal diagonal: query i sees keys 0 .. i + (nk - nq)."""
     if not causal:
@@ -59,15 +68,20 @@ def _causal_offset(nq: int, nk: int, causal: bool) -> int:
 
 
 def _scores(q_rows: np.ndarray, k: np.ndarray, scale: float, causal: bool,
-            row_idx: np.ndarray, col_idx: np.ndarray | None = None, offset: int = 0) -> np.ndarray:
+            row_idx: np.ndarray, col_idx: np.ndarray | None = None, offset: int = 0,
+            window: int = 0) -> np.ndarray:
     """Steps 1-2: scaled scores of the given query rows against keys ``col_idx``
     (all keys when None), with the causal mask applied by global index
-    (key j visible to query i iff j <= i + offset)."""
+    (key j visible to query i iff j <= i + offset, and j > i + offset - window
+    when window > 0)."""
     if col_idx is None:
         col_idx = np.arange(k.shape[0])
     s = scale * (q_rows @ k.T)
     if causal:
-        s = np.where(col_idx[None, :] > row_idx[:, None] + offset, -np.inf, s)
+        hidden = col_idx[None, :] > row_idx[:, None] + offset
+        if window:
+            hidden |= col_idx[None, :] <= row_idx[:, None] + offset - window
+        s = np.where(hidden, -np.inf, s)
     return s
 
 
@@ -79,21 +93,21 @@ def _logsumexp_rows(s: np.ndarray) -> np.ndarray:
     return m + np.log(np.exp(s - m[:, None]).sum(axis=1))
 
 
-def _forward_head(q, k, v, scale, causal, chunk):
+def _forward_head(q, k, v, scale, causal, chunk, window=0):
     n = q.shape[0]
     off = _causal_offset(n, k.shape[0], causal)
     o = np.empty((n, v.shape[1]))
     lse = np.empty(n)
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k, scale, causal, rows, offset=off)
+        s = _scores(q[rows], k, scale, causal, rows, offset=off, window=window)
         lse[rows] = _logsumexp_rows(s)
         p = np.exp(s - lse[rows][:, None])            # step 4
         o[rows] = p @ v                                 # step 5
     return o, lse
 
 
-def _backward_head(q, k, v, do, scale, causal, chunk):
+def _backward_head(q, k, v, do, scale, causal, chunk, window=0):
     n = q.shape[0]
     off = _causal_offset(n, k.shape[0], causal)
     dq = np.zeros_like(q)
@@ -102,7 +116,7 @@ def _backward_head(q, k, v, do, scale, causal, chunk):
     delta = np.empty(n)
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k, scale, causal, rows, offset=off)
+        s = _scores(q[rows], k, scale, causal, rows, offset=off, window=window)
         lse = _logsumexp_rows(s)
         p = np.exp(s - lse[:, None])                    # step 4
         dv += p.T @ do[rows]                            # step 6
@@ -123,21 +137,24 @@ def _batched(fn, arrays, *args):
     return tuple(np.stack(parts) for parts in zip(*outs))
 
 
-def attention_forward(q, k, v, scale=None, causal=False, chunk=DEFAULT_CHUNK):
+def attention_forward(q, k, v, scale=None, causal=False, chunk=DEFAULT_CHUNK, window=0):
     """Return ``(O, L)`` for q of shape [N_q, d] or [BH, N_q, d] and k, v of
-    shape [N_k, d] or [BH, N_k, d] (fp64)."""
+    shape [N_k, d] or [BH, N_k, d] (fp64).  ``window`` > 0 (causal only)
+    limits each query to its ``window`` most recent keys."""
     scale = _default_scale(np.shape(q)[-1], scale)
-    return _batched(_forward_head, (q, k, v), scale, bool(causal), int(chunk))
+    window = _check_window(causal, window)
+    return _batched(_forward_head, (q, k, v), scale, bool(causal), int(chunk), window)
 
 
-def attention_backward(q, k, v, do, scale=None, causal=False, chunk=DEFAULT_CHUNK):
+def attention_backward(q, k, v, do, scale=None, causal=False, chunk=DEFAULT_CHUNK, window=0):
     """Return ``(dQ, dK, dV, D)`` for the loss whose gradient w.r.t. O is dO.
 
     D is computed by its definition ``sum_j P_ij dP_ij``; the forward output
     is not needed.
     """
     scale = _default_scale(np.shape(q)[-1], scale)
-    return _batched(_backward_head, (q, k, v, do), scale, bool(causal), int(chunk))
+    window = _check_window(causal, window)
+    return _batched(_backward_head, (q, k, v, do), scale, bool(causal), int(chunk), window)
 
 
 def delta_from_output(o, do):
@@ -152,24 +169,26 @@ def delta_from_output(o, do):
 # from the same definition, without forming any other row's outputs.
 # --------------------------------------------------------------------------
 
-def forward_rows(q, k, v, rows, scale=None, causal=False):
+def forward_rows(q, k, v, rows, scale=None, causal=False, window=0):
     """O[rows] and L[rows] of one head (q, k, v: [N, d]).  A row of the
     forward depends only on that row's scores."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     scale = _default_scale(q.shape[1], scale)
     rows = np.asarray(rows, dtype=np.int64)
-    s = _scores(q[rows], k, scale, causal, rows, offset=_causal_offset(q.shape[0], k.shape[0], causal))
+    s = _scores(q[rows], k, scale, causal, rows, offset=_causal_offset(q.shape[0], k.shape[0], causal),
+                window=_check_window(causal, window))
     lse = _logsumexp_rows(s)
     return np.exp(s - lse[:, None]) @ v, lse
 
 
-def dq_rows(q, k, v, do, rows, scale=None, causal=False):
+def dq_rows(q, k, v, do, rows, scale=None, causal=False, window=0):
     """dQ[rows] and D[rows] of one head.  Row i of dQ needs only row i of
     S, P, dP and dS (steps 1-4, 7-10)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     scale = _default_scale(q.shape[1], scale)
     rows = np.asarray(rows, dtype=np.int64)
-    s = _scores(q[rows], k, scale, causal, rows, offset=_causal_offset(q.shape[0], k.shape[0], causal))
+    s = _scores(q[rows], k, scale, causal, rows, offset=_causal_offset(q.shape[0], k.shape[0], causal),
+                window=_check_window(causal, window))
     p = np.exp(s - _logsumexp_rows(s)[:, None])
     dp = do[rows] @ v.T
     delta = (p * dp).sum(axis=1)
@@ -177,17 +196,18 @@ def dq_rows(q, k, v, do, rows, scale=None, causal=False):
     return scale * (ds @ k), delta
 
 
-def head_row_stats(q, k, v, do, scale=None, causal=False, chunk=DEFAULT_CHUNK):
+def head_row_stats(q, k, v, do, scale=None, causal=False, chunk=DEFAULT_CHUNK, window=0):
     """L and D for every row of one head (full rows, in chunks)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     scale = _default_scale(q.shape[1], scale)
     n = q.shape[0]
     off = _causal_offset(n, k.shape[0], causal)
+    window = _check_window(causal, window)
     lse = np.empty(n)
     delta = np.empty(n)
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k, scale, causal, rows, offset=off)
+        s = _scores(q[rows], k, scale, causal, rows, offset=off, window=window)
         lse[rows] = _logsumexp_rows(s)
         p = np.exp(s - lse[rows][:, None])
         delta[rows] = (p * (do[rows] @ v.T)).sum(axis=1)
@@ -195,7 +215,7 @@ def head_row_stats(q, k, v, do, scale=None, causal=False, chunk=DEFAULT_CHUNK):
 
 
 def dkdv_cols(q, k, v, do, cols, scale=None, causal=False, stats=None,
-              chunk=DEFAULT_CHUNK):
+              chunk=DEFAULT_CHUNK, window=0):
     """dK[cols] and dV[cols] of one head.  Column j of dK/dV sums over every
     query row, so it needs L_i and D_i of all rows (``stats`` = the pair
     returned by :func:`head_row_stats`; computed here when None) and then only
@@ -204,15 +224,16 @@ def dkdv_cols(q, k, v, do, cols, scale=None, causal=False, stats=None,
     scale = _default_scale(q.shape[1], scale)
     cols = np.asarray(cols, dtype=np.int64)
     if stats is None:
-        stats = head_row_stats(q, k, v, do, scale, causal, chunk)
+        stats = head_row_stats(q, k, v, do, scale, causal, chunk, window)
     lse, delta = stats
     n = q.shape[0]
     off = _causal_offset(n, k.shape[0], causal)
+    window = _check_window(causal, window)
     dk = np.zeros((len(cols), k.shape[1]))
     dv = np.zeros((len(cols), v.shape[1]))
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = _scores(q[rows], k[cols], scale, causal, rows, cols, offset=off)
+        s = _scores(q[rows], k[cols], scale, causal, rows, cols, offset=off, window=window)
         p = np.exp(s - lse[rows][:, None])
         dv += p.T @ do[rows]
         dp = do[rows] @ v[cols].T

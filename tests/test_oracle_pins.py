@@ -499,3 +499,72 @@ def test_rect_pins_catch_a_top_left_mask(monkeypatch):
     monkeypatch.setattr(A, "_causal_offset", lambda nq_, nk_, causal: 0)
     bad, _ = oracle.attention_forward(q, k, v, causal=True)
     assert np.abs(bad - ro).max() > 1e-2
+
+
+# --------------------------------------------------------------------------
+# Sliding window ([CS324-L8] window_attention_torch): with causal masking a
+# query sees only its `window` most recent keys
+# --------------------------------------------------------------------------
+
+def _torch_band_reference(q, k, v, do, window, scale):
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    nq, nk = q.shape[0], k.shape[0]
+    i = torch.arange(nq)[:, None] + (nk - nq)
+    j = torch.arange(nk)[None, :]
+    mask = (j <= i) & (j > i - window)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq[None, None], tk[None, None], tv[None, None], attn_mask=mask, scale=scale)[0, 0]
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    return out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("nq,nk,window", [(64, 64, 5), (64, 64, 16), (30, 100, 7), (1, 50, 10), (50, 50, 200)])
+def test_window_matches_torch_sdpa_band(nq, nk, window):
+    rng = np.random.default_rng(40)
+    d = 8
+    q, do = (rng.standard_normal((nq, d)) for _ in range(2))
+    k, v = (rng.standard_normal((nk, d)) for _ in range(2))
+    scale = 1 / math.sqrt(d)
+    o, lse = oracle.attention_forward(q, k, v, causal=True, window=window, chunk=16)
+    dq, dk, dv, delta = oracle.attention_backward(q, k, v, do, causal=True, window=window, chunk=16)
+    ro, rdq, rdk, rdv = _torch_band_reference(q, k, v, do, window, scale)
+    for a, b in ((o, ro), (dq, rdq), (dk, rdk), (dv, rdv)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * max(1.0, np.abs(b).max()))
+    np.testing.assert_allclose(delta, oracle.delta_from_output(o, do), atol=1e-12)
+
+
+def test_window_special_cases():
+    """window = 1: each query sees only its own position, so O_i = V_{i+off},
+    L_i = S_{i,i+off}, dV_j = dO_{j-off}, and dS = P (dP - D) = 0 gives
+    dQ = dK = 0.  window >= N_k: plain causal attention."""
+    rng = np.random.default_rng(41)
+    nq, nk, d = 20, 35, 8
+    q, do = (rng.standard_normal((nq, d)) for _ in range(2))
+    k, v = (rng.standard_normal((nk, d)) for _ in range(2))
+    off = nk - nq
+    o, lse = oracle.attention_forward(q, k, v, causal=True, window=1)
+    np.testing.assert_allclose(o, v[off:], atol=1e-15)
+    np.testing.assert_allclose(lse, (q * k[off:]).sum(axis=1) / math.sqrt(d), atol=1e-13)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal=True, window=1)
+    np.testing.assert_allclose(dv[off:], do, atol=1e-15)
+    assert np.abs(dv[:off]).max() == 0.0
+    assert np.abs(dq).max() <= 1e-13 and np.abs(dk).max() <= 1e-13
+    full = oracle.attention_forward(q, k, v, causal=True)
+    wide = oracle.attention_forward(q, k, v, causal=True, window=nk)
+    np.testing.assert_allclose(wide[0], full[0], atol=0)
+    with pytest.raises(ValueError):
+        oracle.attention_forward(q, k, v, causal=False, window=4)
+    with pytest.raises(ValueError):
+        oracle.attention_forward(q, k, v, causal=True, window=-1)
+
+
+def test_window_sampled_outputs_match_full():
+    q, k, v, do = (a[0] for a in make_inputs(1, 200, 16, seed=42))
+    o, lse = oracle.attention_forward(q, k, v, causal=True, window=37)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, causal=True, window=37)
+    rows, cols = np.array([0, 36, 37, 199]), np.array([0, 100, 199])
+    np.testing.assert_allclose(oracle.forward_rows(q, k, v, rows, causal=True, window=37)[0], o[rows], atol=1e-14)
+    np.testing.assert_allclose(oracle.dq_rows(q, k, v, do, rows, causal=True, window=37)[0], dq[rows], atol=1e-13)
+    ck, cv = oracle.dkdv_cols(q, k, v, do, cols, causal=True, window=37)
+    np.testing.assert_allclose(ck, dk[cols], atol=1e-13)
+    np.testing.assert_allclose(cv, dv[cols], atol=1e-13)
