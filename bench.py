@@ -6,7 +6,9 @@ fa_bwd_dkdv, fa_bwd_dq (C ABI of libfa.so) on inputs already resident in HBM.
 Default workload: batch*heads = 32, N = 8192, d = 128, bf16, causal.
 
 Counted FLOPs per head (the metric's convention): forward 4 N^2 d, backward
-10 N^2 d, both halved when causal.  Prints one JSON line (rank 0).
+10 N^2 d, both halved when causal.  With --window W (causal sliding window)
+N^2 / 2 becomes the exact count of visible (query, key) pairs,
+N W - W (W - 1) / 2.  Prints one JSON line (rank 0).
 """
 
 from __future__ import annotations
@@ -27,19 +29,27 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fwd+bwd attention TFLOPS (bf16, causal, N=8192, d=128) + % of MFMA peak"
 
 
-def counted_flops(bh, n, d, causal):
-    half = 0.5 if causal else 1.0
-    fwd = 4.0 * n * n * d * bh * half
-    bwd = 10.0 * n * n * d * bh * half
+def score_pairs(n, causal, window=0):
+    """(query, key) pairs whose scores the method needs, per head: N^2, N^2 / 2
+    when causal (the metric's convention), and with a causal window of W < N
+    keys the exact band count N W - W (W - 1) / 2."""
+    if causal and 0 < window < n:
+        return n * window - window * (window - 1) / 2
+    return n * n * (0.5 if causal else 1.0)
+
+
+def counted_flops(bh, n, d, causal, window=0):
+    pairs = score_pairs(n, causal, window)
+    fwd = 4.0 * pairs * d * bh
+    bwd = 10.0 * pairs * d * bh
     return fwd, bwd
 
 
-def kernel_flops(bh, n, d, causal):
+def kernel_flops(bh, n, d, causal, window=0):
     """Algorithmic MFMA flops per launch of each kernel (the contractions it
-    must perform, halved when causal): fwd S and PV (4 N^2 d); dK/dV kernel
-    S, dP, dV, dK (8 N^2 d); dQ kernel S, dP, dQ (6 N^2 d)."""
-    half = 0.5 if causal else 1.0
-    u = 2.0 * n * n * d * bh * half
+    must perform over the needed score pairs): fwd S and PV (4 N^2 d); dK/dV
+    kernel S, dP, dV, dK (8 N^2 d); dQ kernel S, dP, dQ (6 N^2 d)."""
+    u = 2.0 * score_pairs(n, causal, window) * d * bh
     return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u}
 
 
@@ -84,7 +94,7 @@ def measured_traffic(kernel):
     return None
 
 
-def cpu_baseline(bh, n, d, causal, budget_s=25.0):
+def cpu_baseline(bh, n, d, causal, budget_s=25.0, window=0):
     """The fp64 oracle timed on host cores on a bounded sample of the same
     workload: whole heads (forward + backward) until about `budget_s`."""
     import numpy as np
@@ -98,13 +108,13 @@ def cpu_baseline(bh, n, d, causal, budget_s=25.0):
     heads = 0
     t0 = time.perf_counter()
     while True:
-        oracle.attention_forward(q, k, v, causal=causal)
-        oracle.attention_backward(q, k, v, do, causal=causal)
+        oracle.attention_forward(q, k, v, causal=causal, window=window)
+        oracle.attention_backward(q, k, v, do, causal=causal, window=window)
         heads += 1
         el = time.perf_counter() - t0
         if el >= budget_s or el / heads * (heads + 1) > budget_s * 1.5:
             break
-    fwd, bwd = counted_flops(heads, n, d, causal)
+    fwd, bwd = counted_flops(heads, n, d, causal, window)
     threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -116,7 +126,8 @@ def cpu_baseline(bh, n, d, causal, budget_s=25.0):
         "unit": "TFLOPS",
         "cores": threads or cores,
         "kind": "oracle",
-        "sample": f"{heads} of {bh} heads (N={n}, d={d}, {'causal' if causal else 'non-causal'}), "
+        "sample": f"{heads} of {bh} heads (N={n}, d={d}, {'causal' if causal else 'non-causal'}"
+                  f"{f', window {window}' if window else ''}), "
                   f"fp64 fwd+bwd, {el:.1f} s; host cores available: {cores}",
         "seconds": el,
     }
@@ -155,6 +166,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline_8192_d128")
     ap.add_argument("--non-causal", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="causal sliding window of this many keys (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--fwd-tiles", default="0,0")
@@ -193,12 +206,16 @@ def main():
 
     w = WORKLOADS[args.workload]
     causal = not args.non_causal
+    window = args.window
+    if window and not causal:
+        ap.error("--window needs causal attention")
     bh, n, d = w.bh, w.n, w.d
     elt = 2 if w.dtype == "bf16" else 4
     ft = tuple(int(x) for x in args.fwd_tiles.split(","))
     kt = tuple(int(x) for x in args.dkdv_tiles.split(","))
     qt = tuple(int(x) for x in args.dq_tiles.split(","))
-    print(f"# workload {w.name}: bh={bh} n={n} d={d} {w.dtype} causal={causal}", file=sys.stderr, flush=True)
+    print(f"# workload {w.name}: bh={bh} n={n} d={d} {w.dtype} causal={causal} window={window}",
+          file=sys.stderr, flush=True)
 
     q, k, v, do = cast_io(make_inputs(bh, n, d, seed=0), w.dtype, "cuda")
     o = torch.empty_like(q)
@@ -210,19 +227,39 @@ def main():
 
     names = ("fwd", "preprocess", "dkdv", "dq")
 
+    if window:
+        def fwd_call():
+            fa.fa_fwd_rect(q, k, v, o, lse, causal, None, *ft, stream=sptr, window=window)
+
+        def dkdv_call():
+            fa.fa_bwd_dkdv_rect(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr,
+                                window=window)
+
+        def dq_call():
+            fa.fa_bwd_dq_rect(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr, window=window)
+    else:
+        def fwd_call():
+            fa.fa_fwd(q, k, v, o, lse, causal, None, *ft, stream=sptr)
+
+        def dkdv_call():
+            fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr)
+
+        def dq_call():
+            fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, causal, None, *ft, stream=sptr)
+        fwd_call()
         if ev is not None:
             ev[1].record(stream)
         fa.fa_bwd_preprocess(o, do, delta, stream=sptr)
         if ev is not None:
             ev[2].record(stream)
-        fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr)
+        dkdv_call()
         if ev is not None:
             ev[3].record(stream)
-        fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr)
+        dq_call()
         if ev is not None:
             ev[4].record(stream)
 
@@ -249,14 +286,14 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = sum(step_ms) / len(step_ms)
 
-    fwd_fl, bwd_fl = counted_flops(bh, n, d, causal)
+    fwd_fl, bwd_fl = counted_flops(bh, n, d, causal, window)
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     tflops = (fwd_fl + bwd_fl) / (ms_per_step * 1e-3) / 1e12
     fwd_tf = fwd_fl / (avg["fwd"] * 1e-3) / 1e12
     bwd_ms = avg["preprocess"] + avg["dkdv"] + avg["dq"]
     bwd_tf = bwd_fl / (bwd_ms * 1e-3) / 1e12
 
-    kfl = kernel_flops(bh, n, d, causal)
+    kfl = kernel_flops(bh, n, d, causal, window)
     kby = kernel_bytes(bh, n, d, elt)
     dom = max(("fwd", "dkdv", "dq"), key=lambda nm: avg[nm])
     achieved = kfl[dom] / (avg[dom] * 1e-3) / 1e12
@@ -268,8 +305,8 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
         "traffic": (measured_traffic(dom)
-                    if (w.name == "headline_8192_d128" and causal and ft == (0, 0) and kt == (0, 0)
-                        and qt == (0, 0)) else None),
+                    if (w.name == "headline_8192_d128" and causal and not window and ft == (0, 0)
+                        and kt == (0, 0) and qt == (0, 0)) else None),
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
         "avg_launch_ms": round(avg[dom], 4),
         "algorithmic_flops_per_launch": kfl[dom],
@@ -286,7 +323,7 @@ def main():
     base = None
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        base = cpu_baseline(bh, n, d, causal, args.cpu_budget)
+        base = cpu_baseline(bh, n, d, causal, args.cpu_budget, window)
 
     out = {
         "metric": METRIC,
@@ -302,7 +339,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: seeded N(0,1) Q, K, V, dO (numpy default_rng(0), cast to bf16)",
         "config": {"workload": w.name, "batch_heads": bh, "seq_len": n, "head_dim": d,
-                   "causal": causal, "tiles": {"fwd": list(ft), "dkdv": list(kt), "dq": list(qt)}},
+                   "causal": causal, "window": window, "tiles": {"fwd": list(ft), "dkdv": list(kt), "dq": list(qt)}},
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
         "fwd_tflops": round(fwd_tf, 1),
         "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),

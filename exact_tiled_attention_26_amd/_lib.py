@@ -27,9 +27,9 @@ SIGNATURES = {
     "fa_bwd_preprocess": [_P, _P, _P, _I, _I, _I, _I, _P],
     "fa_bwd_dkdv": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P],
     "fa_bwd_dq": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P],
-    "fa_fwd_rect": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P],
-    "fa_bwd_dkdv_rect": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P],
-    "fa_bwd_dq_rect": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P],
+    "fa_fwd_rect": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
+    "fa_bwd_dkdv_rect": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
+    "fa_bwd_dq_rect": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
     "fa_default_tiles": [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "fa_status_str": [_I],
     "fa_abi_version": [],
@@ -191,22 +191,23 @@ def _kv_shape(q, k):
 
 
 def fa_fwd_rect(q, k, v, o, lse, causal: bool, scale: float | None = None,
-                block_m: int = 0, block_n: int = 0, stream=None):
+                block_m: int = 0, block_n: int = 0, stream=None, window: int = 0):
     """Forward for q [bh, nq, d] against k, v [bh, nk, d]; causal masking is
-    aligned to the end of the keys (see include/fa.h)."""
+    aligned to the end of the keys, and ``window`` > 0 (causal only) keeps
+    each query's ``window`` most recent keys (see include/fa.h)."""
     bh, nq, d = _shape3(q)
     nk = _kv_shape(q, k)
     _check_io(q, [("q", q, "io"), ("k", k, "kv"), ("v", v, "kv"), ("o", o, "io"), ("lse", lse, "row")],
               None, kref=k)
     scale = default_scale(d) if scale is None else float(scale)
     st = load_library().fa_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), bh, nq, nk, d,
-                                    _dtype_code(q), scale, int(bool(causal)), int(block_m), int(block_n),
-                                    _stream(stream))
+                                    _dtype_code(q), scale, int(bool(causal)), int(window), int(block_m),
+                                    int(block_n), _stream(stream))
     _check("fa_fwd_rect", st)
 
 
 def fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, causal: bool, scale: float | None = None,
-                     block_m: int = 0, block_n: int = 0, stream=None):
+                     block_m: int = 0, block_n: int = 0, stream=None, window: int = 0):
     """dK, dV for q, dO [bh, nq, d] against k, v [bh, nk, d]."""
     bh, nq, d = _shape3(q)
     nk = _kv_shape(q, k)
@@ -215,12 +216,13 @@ def fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, causal: bool, scale: float
     scale = default_scale(d) if scale is None else float(scale)
     st = load_library().fa_bwd_dkdv_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
                                          _ptr(dk), _ptr(dv), bh, nq, nk, d, _dtype_code(q), scale,
-                                         int(bool(causal)), int(block_m), int(block_n), _stream(stream))
+                                         int(bool(causal)), int(window), int(block_m), int(block_n),
+                                         _stream(stream))
     _check("fa_bwd_dkdv_rect", st)
 
 
 def fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, causal: bool, scale: float | None = None,
-                   block_m: int = 0, block_n: int = 0, stream=None):
+                   block_m: int = 0, block_n: int = 0, stream=None, window: int = 0):
     """dQ for q, dO [bh, nq, d] against k, v [bh, nk, d]."""
     bh, nq, d = _shape3(q)
     nk = _kv_shape(q, k)
@@ -229,33 +231,38 @@ def fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, causal: bool, scale: float | Non
     scale = default_scale(d) if scale is None else float(scale)
     st = load_library().fa_bwd_dq_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta),
                                        _ptr(dq), bh, nq, nk, d, _dtype_code(q), scale, int(bool(causal)),
-                                       int(block_m), int(block_n), _stream(stream))
+                                       int(window), int(block_m), int(block_n), _stream(stream))
     _check("fa_bwd_dq_rect", st)
 
 
 # ------------------------------------------------------------------ allocating helpers
-def forward(q, k, v, causal: bool, scale=None, block_m=0, block_n=0, stream=None):
+def forward(q, k, v, causal: bool, scale=None, block_m=0, block_n=0, stream=None, window=0):
     """Allocate O and L with torch and run fa_fwd (fa_fwd_rect when k has a
-    different length than q); returns (o, lse)."""
+    different length than q or a window is set); returns (o, lse)."""
     import torch
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    fwd = fa_fwd if tuple(k.shape) == tuple(q.shape) else fa_fwd_rect
-    fwd(q, k, v, o, lse, causal, scale, block_m, block_n, stream)
+    if tuple(k.shape) == tuple(q.shape) and not window:
+        fa_fwd(q, k, v, o, lse, causal, scale, block_m, block_n, stream)
+    else:
+        fa_fwd_rect(q, k, v, o, lse, causal, scale, block_m, block_n, stream, window=window)
     return o, lse
 
 
 def backward(q, k, v, o, dO, lse, causal: bool, scale=None, tiles_dkdv=(0, 0), tiles_dq=(0, 0),
-             stream=None):
+             stream=None, window=0):
     """Allocate D, dQ, dK, dV with torch and run the three backward calls in
     order on one stream; returns (dq, dk, dv, delta)."""
     import torch
     delta = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    square = tuple(k.shape) == tuple(q.shape)
     fa_bwd_preprocess(o, dO, delta, stream)
-    (fa_bwd_dkdv if square else fa_bwd_dkdv_rect)(q, k, v, dO, lse, delta, dk, dv, causal, scale,
-                                                  *tiles_dkdv, stream=stream)
-    (fa_bwd_dq if square else fa_bwd_dq_rect)(q, k, v, dO, lse, delta, dq, causal, scale, *tiles_dq,
-                                              stream=stream)
+    if tuple(k.shape) == tuple(q.shape) and not window:
+        fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, causal, scale, *tiles_dkdv, stream=stream)
+        fa_bwd_dq(q, k, v, dO, lse, delta, dq, causal, scale, *tiles_dq, stream=stream)
+    else:
+        fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, causal, scale, *tiles_dkdv, stream=stream,
+                         window=window)
+        fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, causal, scale, *tiles_dq, stream=stream,
+                       window=window)
     return dq, dk, dv, delta

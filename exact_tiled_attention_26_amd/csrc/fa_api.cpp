@@ -62,9 +62,14 @@ fa_status check_common(int bh, int nq, int nk, int d, fa_dtype dtype) {
   return FA_OK;
 }
 
-// Query/key lengths of an attention call: sets `empty` for a no-op call;
-// rejects rows without keys (one length zero, or causal with nq > nk).
-fa_status check_lengths(int bh, int nq, int nk, int causal, bool& empty) {
+// Query/key lengths and window of an attention call: sets `empty` for a
+// no-op call; rejects rows without keys (one length zero, or causal with
+// nq > nk) and a window without causal masking.  A window of nk keys or
+// more hides nothing and is cleared, which also keeps the kernels' window
+// bounds (row + nk - nq - window) far from overflow.
+fa_status check_lengths(int bh, int nq, int nk, int causal, int& window, bool& empty) {
+  if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
+  if (window >= nk) window = 0;
   empty = bh == 0 || (nq == 0 && nk == 0);
   if (empty) return FA_OK;
   if (nq == 0 || nk == 0) return FA_ERR_INVALID_ARG;
@@ -135,30 +140,30 @@ fa_status fa_default_tiles(fa_dtype dtype, int d, int kernel, int* block_m, int*
 
 fa_status fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
                       int bh, int nq, int nk, int d, fa_dtype dtype, float scale, int causal,
-                      int block_m, int block_n, void* stream) {
+                      int window, int block_m, int block_n, void* stream) {
   fa_status s = check_common(bh, nq, nk, d, dtype);
   if (s != FA_OK) return s;
   if ((s = check_scale(scale)) != FA_OK) return s;
   if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
   if ((s = resolve_tiles(dtype, kFwd, d, block_m, block_n)) != FA_OK) return s;
   bool empty = false;
-  if ((s = check_lengths(bh, nq, nk, causal, empty)) != FA_OK || empty) return s;
+  if ((s = check_lengths(bh, nq, nk, causal, window, empty)) != FA_OK || empty) return s;
   if ((s = check_grid(bh, nq, block_m)) != FA_OK) return s;
   if ((s = check_ptrs(q, k, v, o, lse)) != FA_OK) return s;
   if (any_equal({o, lse}, {q, k, v, o, lse})) return FA_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == FA_BF16)
     return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, bh, nq, nk, d, scale, causal != 0,
-                                        block_m, block_n, st));
+                                        window, block_m, block_n, st));
   return from_hip(fa::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v,
-                                     (float*)o, lse, bh, nq, nk, d, scale, causal != 0, block_m,
-                                     block_n, st));
+                                     (float*)o, lse, bh, nq, nk, d, scale, causal != 0, window,
+                                     block_m, block_n, st));
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int bh, int n, int d, fa_dtype dtype, float scale, int causal,
                  int block_m, int block_n, void* stream) {
-  return fa_fwd_rect(q, k, v, o, lse, bh, n, n, d, dtype, scale, causal, block_m, block_n,
+  return fa_fwd_rect(q, k, v, o, lse, bh, n, n, d, dtype, scale, causal, 0, block_m, block_n,
                      stream);
 }
 
@@ -177,62 +182,62 @@ fa_status fa_bwd_preprocess(const void* o, const void* dO, float* delta,
 fa_status fa_bwd_dkdv_rect(const void* q, const void* k, const void* v, const void* dO,
                            const float* lse, const float* delta, void* dk, void* dv,
                            int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
-                           int causal, int block_m, int block_n, void* stream) {
+                           int causal, int window, int block_m, int block_n, void* stream) {
   fa_status s = check_common(bh, nq, nk, d, dtype);
   if (s != FA_OK) return s;
   if ((s = check_scale(scale)) != FA_OK) return s;
   if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
   if ((s = resolve_tiles(dtype, kDkdv, d, block_m, block_n)) != FA_OK) return s;
   bool empty = false;
-  if ((s = check_lengths(bh, nq, nk, causal, empty)) != FA_OK || empty) return s;
+  if ((s = check_lengths(bh, nq, nk, causal, window, empty)) != FA_OK || empty) return s;
   if ((s = check_grid(bh, nk, block_n)) != FA_OK) return s;
   if ((s = check_ptrs(q, k, v, dO, lse, delta, dk, dv)) != FA_OK) return s;
   if (any_equal({dk, dv}, {q, k, v, dO, lse, delta, dk, dv})) return FA_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == FA_BF16)
     return from_hip(fa::launch_dkdv_bf16(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, d, scale,
-                                         causal != 0, block_m, block_n, st));
+                                         causal != 0, window, block_m, block_n, st));
   return from_hip(fa::launch_dkdv_f32((const float*)q, (const float*)k, (const float*)v,
                                       (const float*)dO, lse, delta, (float*)dk, (float*)dv, bh,
-                                      nq, nk, d, scale, causal != 0, block_m, block_n, st));
+                                      nq, nk, d, scale, causal != 0, window, block_m, block_n, st));
 }
 
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                       const float* lse, const float* delta, void* dk, void* dv,
                       int bh, int n, int d, fa_dtype dtype, float scale, int causal,
                       int block_m, int block_n, void* stream) {
-  return fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, bh, n, n, d, dtype, scale, causal,
+  return fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, bh, n, n, d, dtype, scale, causal, 0,
                           block_m, block_n, stream);
 }
 
 fa_status fa_bwd_dq_rect(const void* q, const void* k, const void* v, const void* dO,
                          const float* lse, const float* delta, void* dq,
                          int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
-                         int causal, int block_m, int block_n, void* stream) {
+                         int causal, int window, int block_m, int block_n, void* stream) {
   fa_status s = check_common(bh, nq, nk, d, dtype);
   if (s != FA_OK) return s;
   if ((s = check_scale(scale)) != FA_OK) return s;
   if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
   if ((s = resolve_tiles(dtype, kDq, d, block_m, block_n)) != FA_OK) return s;
   bool empty = false;
-  if ((s = check_lengths(bh, nq, nk, causal, empty)) != FA_OK || empty) return s;
+  if ((s = check_lengths(bh, nq, nk, causal, window, empty)) != FA_OK || empty) return s;
   if ((s = check_grid(bh, nq, block_m)) != FA_OK) return s;
   if ((s = check_ptrs(q, k, v, dO, lse, delta, dq)) != FA_OK) return s;
   if (any_equal({dq}, {q, k, v, dO, lse, delta, dq})) return FA_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == FA_BF16)
     return from_hip(fa::launch_dq_bf16(q, k, v, dO, lse, delta, dq, bh, nq, nk, d, scale,
-                                       causal != 0, block_m, block_n, st));
+                                       causal != 0, window, block_m, block_n, st));
   return from_hip(fa::launch_dq_f32((const float*)q, (const float*)k, (const float*)v,
                                     (const float*)dO, lse, delta, (float*)dq, bh, nq, nk, d,
-                                    scale, causal != 0, block_m, block_n, st));
+                                    scale, causal != 0, window, block_m, block_n, st));
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                     const float* lse, const float* delta, void* dq,
                     int bh, int n, int d, fa_dtype dtype, float scale, int causal,
                     int block_m, int block_n, void* stream) {
-  return fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, bh, n, n, d, dtype, scale, causal,
+  return fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, bh, n, n, d, dtype, scale, causal, 0,
                         block_m, block_n, stream);
 }
 

@@ -46,7 +46,8 @@ __device__ __forceinline__ void rows_load_async(float* lds, const float* src, in
 }
 
 // nq query rows attend to nk key rows; causal masking is aligned to the end
-// of the key sequence (query i sees keys 0 .. i + nk - nq).
+// of the key sequence (query i sees keys 0 .. i + nk - nq), and a window > 0
+// hides keys at or below i + nk - nq - window.
 // RAGGED: nq may not be a multiple of BR (the last query tile needs the mask).
 template <int D, int KW, int NW, int BR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(NW * 64, 1)
@@ -54,7 +55,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ DELTA,
                       __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                      int bh, int nq, int nk, float scale, float scale_log2) {
+                      int bh, int nq, int nk, int window, float scale, float scale_log2) {
   constexpr int BC = KW * NW;
   constexpr int NKB = KW / 16;   // 16-key blocks per wave
   constexpr int NDS = D / 32;
@@ -75,6 +76,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int k0 = kt * BC;
   const int k0w = k0 + wave * KW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
   const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
   const __bf16* Qh = Q + hoffq;
   const __bf16* dOh = dO + hoffq;
@@ -83,6 +85,8 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   const int ntq = (nq + BR - 1) / BR;
   const int it0 = CAUSAL ? max(0, k0 - off) / BR : 0;   // earlier query rows see none of these keys
+  // later rows see none of them either once the window has moved past them
+  const int it1 = CAUSAL ? min(ntq, max(0, k0 + BC - 2 - lo) / BR + 1) : ntq;
   // compiler-visible copies: measured faster than the hidden form here
   const AsyncTileCopy<D, BR, NW, false> copier(wave, lane);
   auto issue_tile = [&](__bf16* qd, __bf16* od, float* ld, float* dd, int i0) __attribute__((always_inline)) {
@@ -175,9 +179,10 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       for (int i = 0; i < 4; ++i) {
         const int q = i0 + 32 * t + 16 * h + 4 * g + i;
         const int lim = (q < nq) ? (CAUSAL ? q + off - k0w - l16 : 0x7fffffff) : -1;
+        const int llim = q + lo - k0w - l16;   // key 16kb + .. hidden from below iff 16kb <= llim
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          if (16 * kb > lim) {
+          if (16 * kb > lim || (CAUSAL && 16 * kb <= llim)) {
             e.pv[h][kb][i] = 0.f;
             e.dsv[h][kb][i] = 0.f;
           }
@@ -304,12 +309,14 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   auto tile_step = [&](const __bf16* qt, const __bf16* ot, const float* lt, const float* dt,
                        __bf16* qn, __bf16* on, float* ln, float* dn, int it) __attribute__((always_inline)) {
     const int i0 = it * BR;
-    if (it + 1 < ntq) issue_tile(qn, on, ln, dn, i0 + BR);
-    const bool active = !CAUSAL || (i0 + BR - 1 + off >= k0w);
+    if (it + 1 < it1) issue_tile(qn, on, ln, dn, i0 + BR);
+    const bool active = !CAUSAL || (i0 + BR - 1 + off >= k0w && i0 + lo < k0w + KW - 1);
     if (active) {
-      // only tiles crossing the diagonal or the end of the sequence are masked;
-      // they run a separate copy so that the others carry no mask arithmetic
-      if ((CAUSAL || RAGGED) && ((CAUSAL && i0 + off < k0w + KW - 1) || (i0 + BR > nq))) {
+      // only tiles crossing the diagonal, the window's edge or the end of the
+      // sequence are masked; they run a separate copy so that the others carry
+      // no mask arithmetic
+      if ((CAUSAL || RAGGED) &&
+          ((CAUSAL && (i0 + off < k0w + KW - 1 || i0 + BR - 1 + lo >= k0w)) || (i0 + BR > nq))) {
         run_tile(qt, ot, lt, dt, i0, std::true_type{});
       } else {
         run_tile(qt, ot, lt, dt, i0, std::false_type{});
@@ -320,9 +327,9 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   };
 
 #pragma unroll 1
-  for (int it = it0; it < ntq; it += 2) {
+  for (int it = it0; it < it1; it += 2) {
     tile_step(q_lds0, o_lds0, l_lds0, d_lds0, q_lds1, o_lds1, l_lds1, d_lds1, it);
-    if (it + 1 < ntq) tile_step(q_lds1, o_lds1, l_lds1, d_lds1, q_lds0, o_lds0, l_lds0, d_lds0, it + 1);
+    if (it + 1 < it1) tile_step(q_lds1, o_lds1, l_lds1, d_lds1, q_lds0, o_lds0, l_lds0, d_lds0, it + 1);
   }
 
   // write dK = scale * dK_acc and dV
@@ -350,7 +357,8 @@ __global__ __launch_bounds__(NW * 64, 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                     const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                    __bf16* __restrict__ dQ, int bh, int nq, int nk, float scale, float scale_log2) {
+                    __bf16* __restrict__ dQ, int bh, int nq, int nk, int window, float scale,
+                    float scale_log2) {
   constexpr int BR = QW * NW;
   constexpr int NQB = QW / 16;
   constexpr int NKB = BC / 16;
@@ -370,16 +378,18 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
   const size_t hoffq = (size_t)head * nq * D;
   const __bf16* Kh = K + (size_t)head * nk * D;
   const __bf16* Vh = V + (size_t)head * nk * D;
 
   const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
+  const int jt0 = max(0, q0 + lo + 1) / BC;   // first key tile a row of the workgroup can see
   const int ntk = (kend + BC - 1) / BC;
   // compiler-visible copies: measured faster than the hidden form here
   const AsyncTileCopy<D, BC, NW, false> copier(wave, lane);
-  copier.issue(k_lds0, Kh, min(BC, nk));
-  copier.issue(v_lds0, Vh, min(BC, nk));
+  copier.issue(k_lds0, Kh + (size_t)jt0 * BC * D, nk - jt0 * BC);
+  copier.issue(v_lds0, Vh + (size_t)jt0 * BC * D, nk - jt0 * BC);
 
   bf16x8 qf[NQB][NDS], of[NQB][NDS];
   float l2q[NQB], dq_d[NQB];
@@ -418,7 +428,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       copier.issue(kn, Kh + (size_t)(j0 + BC) * D, nk - j0 - BC);
       copier.issue(vn, Vh + (size_t)(j0 + BC) * D, nk - j0 - BC);
     }
-    const bool active = !CAUSAL || (j0 <= q0w + QW - 1 + off);
+    const bool active = !CAUSAL || (j0 <= q0w + QW - 1 + off && j0 + BC - 1 > q0w + lo);
     if (active) {
       // S^T = K Q^T, dP^T = V dO^T: lane holds key 16kb + 4g + i, query 16qb + l16
       f32x4 s[NKB][NQB], dp[NKB][NQB];
@@ -455,7 +465,8 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool need_mask = (CAUSAL && j0 + BC - 1 > q0w + off) || (j0 + BC > nk);
+      const bool need_mask = (CAUSAL && (j0 + BC - 1 > q0w + off || j0 <= q0w + QW - 1 + lo)) ||
+                             (j0 + BC > nk);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -471,12 +482,14 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const int last = CAUSAL ? min(q0w + 16 * qb + l16 + off, nk - 1) : nk - 1;
-          const int lim = last - j0 - 4 * g;   // key j0 + 16kb + 4g + i visible iff 16kb + i <= lim
+          // key j0 + 16kb + 4g + i visible iff llim < 16kb + i <= lim
+          const int lim = last - j0 - 4 * g;
+          const int llim = q0w + 16 * qb + l16 + lo - j0 - 4 * g;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (16 * kb + i > lim) dp[kb][qb][i] = 0.f;
+              if (16 * kb + i > lim || (CAUSAL && 16 * kb + i <= llim)) dp[kb][qb][i] = 0.f;
         }
       }
       // dQ^T += K^T dS^T (Eq 18, scale applied at the end)
@@ -510,7 +523,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   };
 
 #pragma unroll 1
-  for (int j = 0; j < ntk; j += 2) {
+  for (int j = jt0; j < ntk; j += 2) {
     tile_step(k_lds0, v_lds0, k_lds1, v_lds1, j);
     if (j + 1 < ntk) tile_step(k_lds1, v_lds1, k_lds0, v_lds0, j + 1);
   }
@@ -533,7 +546,8 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 template <int D, int KW, int NW, int BR>
 static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, const void* dO,
                                    const float* lse, const float* delta, void* dk, void* dv,
-                                   int bh, int nq, int nk, float scale, int causal, hipStream_t st) {
+                                   int bh, int nq, int nk, float scale, int causal, int window,
+                                   hipStream_t st) {
   constexpr int BC = KW * NW;
   const int ntk = (nk + BC - 1) / BC;
   const dim3 grid((unsigned)(ntk * bh)), block(NW * 64);
@@ -544,14 +558,16 @@ static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, 
   auto kern = causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true>
                      : dkdv_bf16_kernel<D, KW, NW, BR, false, true>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, bh, nq, nk, scale, sl2);
+                     (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, bh, nq, nk, window, scale,
+                     sl2);
   return hipGetLastError();
 }
 
 template <int D, int QW, int NW, int BC>
 static hipError_t launch_dq_inst(const void* q, const void* k, const void* v, const void* dO,
                                  const float* lse, const float* delta, void* dq,
-                                 int bh, int nq, int nk, float scale, int causal, hipStream_t st) {
+                                 int bh, int nq, int nk, float scale, int causal, int window,
+                                 hipStream_t st) {
   constexpr int BR = QW * NW;
   const int ntq = (nq + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
@@ -559,11 +575,11 @@ static hipError_t launch_dq_inst(const void* q, const void* k, const void* v, co
   if (causal) {
     hipLaunchKernelGGL((dq_bf16_kernel<D, QW, NW, BC, true>), grid, block, 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dq, bh, nq, nk, scale, sl2);
+                       lse, delta, (__bf16*)dq, bh, nq, nk, window, scale, sl2);
   } else {
     hipLaunchKernelGGL((dq_bf16_kernel<D, QW, NW, BC, false>), grid, block, 0, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dq, bh, nq, nk, scale, sl2);
+                       lse, delta, (__bf16*)dq, bh, nq, nk, window, scale, sl2);
   }
   return hipGetLastError();
 }
@@ -571,26 +587,26 @@ static hipError_t launch_dq_inst(const void* q, const void* k, const void* v, co
 // dK/dV tilings: block_m = query rows per inner step, block_n = keys per workgroup.
 hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO,
                             const float* lse, const float* delta, void* dk, void* dv,
-                            int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                            int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                             hipStream_t st) {
   if (d == 128 && bm == 64 && bn == 128)
-    return launch_dkdv_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, st);
+    return launch_dkdv_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, window, st);
   if (d == 128 && bm == 128 && bn == 128)
-    return launch_dkdv_inst<128, 32, 4, 128>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, st);
+    return launch_dkdv_inst<128, 32, 4, 128>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, window, st);
   if (d == 64 && bm == 64 && bn == 128)
-    return launch_dkdv_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, st);
+    return launch_dkdv_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, window, st);
   return hipErrorInvalidValue;
 }
 
 // dQ tilings: block_m = queries per workgroup, block_n = keys per inner step.
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO,
                           const float* lse, const float* delta, void* dq,
-                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                           hipStream_t st) {
   if (d == 128 && bm == 128 && bn == 64)
-    return launch_dq_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, st);
+    return launch_dq_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   if (d == 64 && bm == 128 && bn == 64)
-    return launch_dq_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, st);
+    return launch_dq_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   return hipErrorInvalidValue;
 }
 

@@ -80,6 +80,12 @@ __device__ __forceinline__ int divergent_zero() {
   return z;
 }
 
+// Lower edge of the visible keys: key j is hidden from query i when
+// j <= i + lo.  Without a window no key is hidden from below.
+__device__ __forceinline__ int window_lo(bool causal, int off, int window) {
+  return (causal && window > 0) ? off - window : -(1 << 30);
+}
+
 // Pack two 4-float accumulator fragments into one bf16x8 operand
 // (round to nearest even).
 __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {

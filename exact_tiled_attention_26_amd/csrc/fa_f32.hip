@@ -33,7 +33,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512)
 void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                     const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-                    int bh, int nq, int nk, float scale_log2, int BR, int BC) {
+                    int bh, int nq, int nk, int window, float scale_log2, int BR, int BC) {
   extern __shared__ float smem[];
   constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
   const int BCP = (BC + 15) & ~15, nkb = BCP / 16;
@@ -47,6 +47,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int q0w = q0 + 16 * wave;
   const int qr = q0w + l16;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
   const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
 
   // B operand of S^T = K Q^T: lane holds Q[qr][4st + g]
@@ -60,14 +61,15 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
   const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
   const int ntk = (kend + BC - 1) / BC;
-  for (int j = 0; j < ntk; ++j) {
+  const int jt0 = max(0, q0 + lo + 1) / BC;   // first key tile any row can see
+  for (int j = jt0; j < ntk; ++j) {
     const int j0 = j * BC;
     const int valid = min(BC, nk - j0);
     __syncthreads();
     stage_f32_rows<D>(ks, K + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
     stage_f32_rows<D>(vs, V + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
     __syncthreads();
-    if (CAUSAL && j0 > q0w + 15 + off) continue;
+    if (CAUSAL && (j0 > q0w + 15 + off || j0 + BC - 1 <= q0w + lo)) continue;
     // S^T: lane holds key j0 + 16kb + 4g + i, query qr
     f32x4 s[kMaxBlk];
     float mx = kNegInf;
@@ -80,7 +82,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kl = 16 * kb + 4 * g + i;
-          if (kl >= valid || (CAUSAL && j0 + kl > qr + off)) c[i] = kNegInf;
+          if (kl >= valid || (CAUSAL && (j0 + kl > qr + off || j0 + kl <= qr + lo))) c[i] = kNegInf;
           mx = fmaxf(mx, c[i]);
         }
         s[kb] = c;
@@ -137,7 +139,7 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                      const float* __restrict__ V, const float* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ DELTA,
                      float* __restrict__ dK, float* __restrict__ dV,
-                     int bh, int nq, int nk, float scale, float scale_log2, int BR, int BC) {
+                     int bh, int nq, int nk, int window, float scale, float scale_log2, int BR, int BC) {
   extern __shared__ float smem[];
   constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
   float* qs = smem;
@@ -153,6 +155,7 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int key = k0w + l16;
   const bool key_ok = key < nk && key < k0 + BC;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
   const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
 
   // B operands of S = Q K^T and dP = dO V^T: lane holds K[key][4st + g], V[key][4st + g]
@@ -170,7 +173,9 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   }
   const int ntq = (nq + BR - 1) / BR;
   const int it0 = CAUSAL ? max(0, k0 - off) / BR : 0;   // earlier queries see none of these keys
-  for (int it = it0; it < ntq; ++it) {
+  // later queries see none of them either once the window has passed them
+  const int it1 = min(ntq, max(0, k0 + BC - 2 - lo) / BR + 1);
+  for (int it = it0; it < it1; ++it) {
     const int i0 = it * BR;
     const int valid = min(BR, nq - i0);
     __syncthreads();
@@ -181,7 +186,7 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       dsm[r] = (r < valid) ? DELTA[(size_t)head * nq + i0 + r] : 0.f;
     }
     __syncthreads();
-    if (CAUSAL && i0 + BR - 1 + off < k0w) continue;
+    if (CAUSAL && (i0 + BR - 1 + off < k0w || i0 + lo >= k0w + 15)) continue;
 #pragma unroll
     for (int qb = 0; qb < kMaxBlk; ++qb) {
       if (qb < nqb) {
@@ -198,7 +203,7 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int i = 0; i < 4; ++i) {
           const int rl = 16 * qb + 4 * g + i;
           float p = exp2_fast(__builtin_fmaf(s[i], scale_log2, -l2s[rl]));
-          if (CAUSAL && key > i0 + rl + off) p = 0.f;
+          if (CAUSAL && (key > i0 + rl + off || key <= i0 + rl + lo)) p = 0.f;
           s[i] = p;
           dp[i] = p * (dp[i] - dsm[rl]);
         }
@@ -230,8 +235,8 @@ __global__ __launch_bounds__(512)
 void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                    const float* __restrict__ V, const float* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                   float* __restrict__ dQ, int bh, int nq, int nk, float scale, float scale_log2,
-                   int BR, int BC) {
+                   float* __restrict__ dQ, int bh, int nq, int nk, int window, float scale,
+                   float scale_log2, int BR, int BC) {
   extern __shared__ float smem[];
   constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
   const int BCP = (BC + 15) & ~15, nkb = BCP / 16;
@@ -245,6 +250,7 @@ void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int q0w = q0 + 16 * wave;
   const int qr = q0w + l16;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
   const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
 
   float qf[NST], of[NST];
@@ -261,14 +267,15 @@ void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
   const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
   const int ntk = (kend + BC - 1) / BC;
-  for (int j = 0; j < ntk; ++j) {
+  const int jt0 = max(0, q0 + lo + 1) / BC;   // first key tile any row can see
+  for (int j = jt0; j < ntk; ++j) {
     const int j0 = j * BC;
     const int valid = min(BC, nk - j0);
     __syncthreads();
     stage_f32_rows<D>(ks, K + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
     stage_f32_rows<D>(vs, V + hoffk + (size_t)j0 * D, BCP, valid, tid, nthr);
     __syncthreads();
-    if (CAUSAL && j0 > q0w + 15 + off) continue;
+    if (CAUSAL && (j0 > q0w + 15 + off || j0 + BC - 1 <= q0w + lo)) continue;
 #pragma unroll
     for (int kb = 0; kb < kMaxBlk; ++kb) {
       if (kb < nkb) {
@@ -285,7 +292,7 @@ void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int i = 0; i < 4; ++i) {
           const int kl = 16 * kb + 4 * g + i;
           float p = exp2_fast(__builtin_fmaf(s[i], scale_log2, -l2q));
-          if (kl >= valid || (CAUSAL && j0 + kl > qr + off)) p = 0.f;
+          if (kl >= valid || (CAUSAL && (j0 + kl > qr + off || j0 + kl <= qr + lo))) p = 0.f;
           dp[i] = p * (dp[i] - dd);
         }
         // dQ^T += K^T dS^T: step t carries key 16kb + 4g + t
@@ -328,7 +335,7 @@ static hipError_t set_lds(KernelT kern, size_t bytes) {
   }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                           hipStream_t st) {
   const size_t lds = f32_lds_bytes(0, d, bm, bn);
   const dim3 grid((unsigned)(((nq + bm - 1) / bm) * bh)), block(bm * 4);
@@ -338,7 +345,8 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
     auto kern = causal ? fwd_f32_kernel<DD, true> : fwd_f32_kernel<DD, false>;              \
     hipError_t e = set_lds(kern, lds);                                                      \
     if (e != hipSuccess) return e;                                                          \
-    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, o, lse, bh, nq, nk, sl2, bm, bn); \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, o, lse, bh, nq, nk, window, sl2,  \
+                       bm, bn);                                                             \
   }
   FA_F32_DISPATCH_D(FA_FWD_F32)
 #undef FA_FWD_F32
@@ -347,7 +355,7 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 
 hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const float* dO,
                            const float* lse, const float* delta, float* dk, float* dv,
-                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                            hipStream_t st) {
   const size_t lds = f32_lds_bytes(1, d, bm, bn);
   const dim3 grid((unsigned)(((nk + bn - 1) / bn) * bh)), block(((bn + 15) / 16) * 64);
@@ -358,7 +366,7 @@ hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const
     hipError_t e = set_lds(kern, lds);                                                      \
     if (e != hipSuccess) return e;                                                          \
     hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dk, dv, bh, nq, \
-                       nk,                                                                  \
+                       nk, window,                                                          \
                        scale, sl2, bm, bn);                                                 \
   }
   FA_F32_DISPATCH_D(FA_DKDV_F32)
@@ -368,7 +376,7 @@ hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const
 
 hipError_t launch_dq_f32(const float* q, const float* k, const float* v, const float* dO,
                          const float* lse, const float* delta, float* dq,
-                         int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                         int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                          hipStream_t st) {
   const size_t lds = f32_lds_bytes(2, d, bm, bn);
   const dim3 grid((unsigned)(((nq + bm - 1) / bm) * bh)), block(bm * 4);
@@ -379,6 +387,7 @@ hipError_t launch_dq_f32(const float* q, const float* k, const float* v, const f
     hipError_t e = set_lds(kern, lds);                                                      \
     if (e != hipSuccess) return e;                                                          \
     hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dq, bh, nq, nk,  \
+                       window,                                                              \
                        scale, sl2, bm, bn);                                                 \
   }
   FA_F32_DISPATCH_D(FA_DQ_F32)

@@ -41,13 +41,15 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kFwdBuffers = 2;   // LDS buffers per operand (copy distance NBUF - 1 tiles)
 
 // nq query rows attend to nk key rows; causal masking is aligned to the end
-// of the key sequence (query i sees keys 0 .. i + nk - nq).
+// of the key sequence (query i sees keys 0 .. i + nk - nq), and a window > 0
+// hides keys at or below i + nk - nq - window.
 // RAGGED: nk may not be a multiple of BC (the last key tile needs the mask).
 template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED, int NBUF>
 __global__ __launch_bounds__(NW * 64, 2)
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                     float* __restrict__ LSE, int bh, int nq, int nk, float scale_log2) {
+                     float* __restrict__ LSE, int bh, int nq, int nk, int window,
+                     float scale_log2) {
   constexpr int BR = QW * NW;
   constexpr int NQB = QW / 16;   // 16-query blocks per wave
   constexpr int NKB = BC / 16;   // 16-key blocks per tile
@@ -75,20 +77,23 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
+  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
   const __bf16* Qh = Q + (size_t)head * nq * D;
   const __bf16* Kh = K + (size_t)head * nk * D;
   const __bf16* Vh = V + (size_t)head * nk * D;
 
   const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;   // keys this workgroup can see
   const int ntk = (kend + BC - 1) / BC;
+  const int jt0 = max(0, q0 + lo + 1) / BC;   // first key tile a row of the workgroup can see
   // last key tile with a key that one of this wave's rows can see
   // (dz: see divergent_zero)
   const int dz = divergent_zero();
   const int last = CAUSAL ? min(ntk - 1, (q0w + QW - 1 + off) / BC) : ntk - 1 + dz;
   const AsyncTileCopy<D, BC, NW> copier(wave, lane);
-  copier.issue(k_lds[0], Kh, min(BC, nk));
-  if (ntk > 1) copier.issue(k_lds[1], Kh + (size_t)BC * D, nk - BC);
-  copier.issue(v_lds[0], Vh, min(BC, nk));
+  // buffers are indexed by the tile's position t - jt0 in the loop
+  copier.issue(k_lds[0], Kh + (size_t)jt0 * BC * D, nk - jt0 * BC);
+  if (jt0 + 1 < ntk) copier.issue(k_lds[1], Kh + (size_t)(jt0 + 1) * BC * D, nk - (jt0 + 1) * BC);
+  copier.issue(v_lds[0], Vh + (size_t)jt0 * BC * D, nk - jt0 * BC);
 
   // Q rows of this wave as B operands: lane holds Q[q0w + 16qb + l16][32ds + 8g .. +7]
   bf16x8 qf[NQB][NDS];
@@ -127,15 +132,17 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // does key tile j need the in-tile mask for this wave?
   auto tile_masked = [&](int j) __attribute__((always_inline)) {
-    return (CAUSAL && j * BC + BC - 1 > q0w + off) || (RAGGED && j * BC + BC > nk + dz);
+    return (CAUSAL && (j * BC + BC - 1 > q0w + off || j * BC <= q0w + QW - 1 + lo)) ||
+           (RAGGED && j * BC + BC > nk + dz);
   };
-  // in-tile mask: key j0 + 16kb + 4g + i is visible iff 16kb + i <= lim
+  // in-tile mask: key j0 + 16kb + 4g + i is visible iff llim < 16kb + i <= lim
   auto mask_item = [&](f32x4 (&s)[NKB][NQB], int j0, int qb, int kb) __attribute__((always_inline)) {
     const int lastq = CAUSAL ? min(q0w + 16 * qb + l16 + off, nk - 1) : nk - 1;
     const int lim = lastq - j0 - 4 * g;
+    const int llim = q0w + 16 * qb + l16 + lo - j0 - 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (16 * kb + i > lim) s[kb][qb][i] = kNegInf;
+      if (16 * kb + i > lim || (CAUSAL && 16 * kb + i <= llim)) s[kb][qb][i] = kNegInf;
   };
   // scaled max (base 2) of one query block over this lane's 16 keys of the
   // tile; the other three lanes of the query hold the rest of the row
@@ -186,16 +193,16 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   async_copy_wait();
   // copies that step 0 waits for when the distance is two steps
   if constexpr (NBUF == 3) {
-    if (ntk > 1) copier.issue(v_lds[1], Vh + (size_t)BC * D, nk - BC);
-    if (ntk > 2) copier.issue(k_lds[2], Kh + (size_t)2 * BC * D, nk - 2 * BC);
+    if (jt0 + 1 < ntk) copier.issue(v_lds[1], Vh + (size_t)(jt0 + 1) * BC * D, nk - (jt0 + 1) * BC);
+    if (jt0 + 2 < ntk) copier.issue(k_lds[2], Kh + (size_t)(jt0 + 2) * BC * D, nk - (jt0 + 2) * BC);
   }
   __syncthreads();
   s_gemm_plain(sa, k_lds[0]);
-  if (tile_masked(0)) {
+  if (tile_masked(jt0)) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mask_item(sa, 0, qb, kb);
+      for (int kb = 0; kb < NKB; ++kb) mask_item(sa, jt0 * BC, qb, kb);
   }
   {
     float mx[NQB];
@@ -310,7 +317,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // t+1 needs and synchronise.
   constexpr int PER = AsyncTileCopy<D, BC, NW>::PER_WAVE;   // copy instructions per tile and wave
   auto step = [&](f32x4 (&sc)[NKB][NQB], f32x4 (&sn)[NKB][NQB], int t) __attribute__((always_inline)) {
-    const int b0 = t % NBUF, b1 = (t + 1) % NBUF, bl = (t + NBUF - 1) % NBUF;
+    const int r = t - jt0;
+    const int b0 = r % NBUF, b1 = (r + 1) % NBUF, bl = (r + NBUF - 1) % NBUF;
     const bool ck = t + NBUF < ntk, cv = t + NBUF - 1 < ntk;
     if (cv) copier.issue(v_lds[bl], Vh + (size_t)(t + NBUF - 1) * BC * D, nk - (t + NBUF - 1) * BC);
     if (ck) copier.issue(k_lds[b0], Kh + (size_t)(t + NBUF) * BC * D, nk - (t + NBUF) * BC);
@@ -338,7 +346,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   };
 
 #pragma unroll 1
-  for (int t = 0; t < ntk; t += 2) {
+  for (int t = jt0; t < ntk; t += 2) {
     step(sa, sb, t);
     if (t + 1 < ntk) step(sb, sa, t + 1);
   }
@@ -365,7 +373,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 template <int D, int QW, int NW, int BC>
 static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, void* o, float* lse,
-                                  int bh, int nq, int nk, float scale, int causal, hipStream_t st) {
+                                  int bh, int nq, int nk, float scale, int causal, int window,
+                                  hipStream_t st) {
   constexpr int BR = QW * NW;
   const int ntq = (nq + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
@@ -374,18 +383,18 @@ static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, v
             : (nk % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, kFwdBuffers>
                        : fwd_bf16_kernel<D, QW, NW, BC, false, false, kFwdBuffers>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (__bf16*)o, lse, bh, nq, nk, sl2);
+                     (__bf16*)o, lse, bh, nq, nk, window, sl2);
   return hipGetLastError();
 }
 
 // Tuned tilings: (head dim, BR, BC) -> instance.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                            hipStream_t st) {
-  if (d == 128 && bm == 128 && bn == 64) return launch_fwd_inst<128, 32, 4, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
-  if (d == 128 && bm == 256 && bn == 64) return launch_fwd_inst<128, 32, 8, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
-  if (d == 64 && bm == 128 && bn == 64) return launch_fwd_inst<64, 32, 4, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
-  if (d == 64 && bm == 256 && bn == 64) return launch_fwd_inst<64, 32, 8, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, st);
+  if (d == 128 && bm == 128 && bn == 64) return launch_fwd_inst<128, 32, 4, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, window, st);
+  if (d == 128 && bm == 256 && bn == 64) return launch_fwd_inst<128, 32, 8, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, window, st);
+  if (d == 64 && bm == 128 && bn == 64) return launch_fwd_inst<64, 32, 4, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, window, st);
+  if (d == 64 && bm == 256 && bn == 64) return launch_fwd_inst<64, 32, 8, 64>(q, k, v, o, lse, bh, nq, nk, scale, causal, window, st);
   return hipErrorInvalidValue;
 }
 

@@ -5,7 +5,8 @@
 // nq query rows (Q, O, dO, dQ, L, D) attend to nk key rows (K, V, dK, dV).
 // Causal masking is aligned to the end of the key sequence: query i sees key
 // j iff j <= i + (nk - nq); the caller guarantees nk >= nq when causal and
-// nq, nk >= 1.
+// nq, nk >= 1.  window > 0 (causal only) also hides keys j <= i + (nk - nq)
+// - window, so that each query sees its `window` most recent keys.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,27 +14,27 @@
 namespace fa {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                            hipStream_t st);
 hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO,
                             const float* lse, const float* delta, void* dk, void* dv,
-                            int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                            int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                             hipStream_t st);
 hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const void* dO,
                           const float* lse, const float* delta, void* dq,
-                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                           hipStream_t st);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                          int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                           hipStream_t st);
 hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const float* dO,
                            const float* lse, const float* delta, float* dk, float* dv,
-                           int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                           int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                            hipStream_t st);
 hipError_t launch_dq_f32(const float* q, const float* k, const float* v, const float* dO,
                          const float* lse, const float* delta, float* dq,
-                         int bh, int nq, int nk, int d, float scale, int causal, int bm, int bn,
+                         int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                          hipStream_t st);
 
 // dtype: 0 = float32, 1 = bf16

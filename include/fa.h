@@ -16,7 +16,8 @@
  *                      the same with nq queries attending to nk keys
  *                      (causal masking aligned to the end of the keys), for
  *                      a chunk of new queries against a longer key/value
- *                      cache; fa_bwd_preprocess serves both forms.
+ *                      cache, and an optional causal sliding window;
+ *                      fa_bwd_preprocess serves both forms.
  *
  * Source of the method (cited by page and section):
  *   "Assignment2: FlashAttention & Distributed Data Parallel notes"
@@ -124,18 +125,24 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
 
 /* The three calls above for nq queries against nk keys (see "Queries and
  * keys of different lengths").  fa_bwd_preprocess(o, dO, delta, bh, nq, d,
- * ...) provides delta. */
+ * ...) provides delta.  window > 0 (only with causal != 0) is a sliding
+ * window ("CS324 lecture 8, 03_online_softmax_and_flash.py",
+ * window_attention_torch): key j is also hidden from query i when
+ * j <= i + (nk - nq) - window, so each query sees its `window` most recent
+ * keys; key tiles wholly outside the band are skipped and only tiles that
+ * cross one of its edges are masked.  window == 0 means no window;
+ * window < 0, or window > 0 without causal, is FA_ERR_INVALID_ARG. */
 fa_status fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
                       int bh, int nq, int nk, int d, fa_dtype dtype, float scale, int causal,
-                      int block_m, int block_n, void* stream);
+                      int window, int block_m, int block_n, void* stream);
 fa_status fa_bwd_dkdv_rect(const void* q, const void* k, const void* v, const void* dO,
                            const float* lse, const float* delta, void* dk, void* dv,
                            int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
-                           int causal, int block_m, int block_n, void* stream);
+                           int causal, int window, int block_m, int block_n, void* stream);
 fa_status fa_bwd_dq_rect(const void* q, const void* k, const void* v, const void* dO,
                          const float* lse, const float* delta, void* dq,
                          int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
-                         int causal, int block_m, int block_n, void* stream);
+                         int causal, int window, int block_m, int block_n, void* stream);
 
 /* The tiling (block_m, block_n) that block_m = block_n = 0 selects for a
  * kernel (0 = fwd, 1 = dkdv, 2 = dq) at this dtype and head dim.  Returns

@@ -147,18 +147,18 @@ def test_tilings(lib):
 
 def rect(lib, fn, **kw):
     a = dict(q=A, k=B, v=C, dO=D_, lse=E, delta=F, o=D_, dq=G, dk=G, dv=H, bh=1, nq=64, nk=128, d=64,
-             dtype=fa.FA_BF16, scale=0.125, causal=1, bm=0, bn=0)
+             dtype=fa.FA_BF16, scale=0.125, causal=1, window=0, bm=0, bn=0)
     a.update(kw)
     if fn == "fwd":
         return lib.fa_fwd_rect(a["q"], a["k"], a["v"], a["o"], a["lse"], a["bh"], a["nq"], a["nk"], a["d"],
-                               a["dtype"], a["scale"], a["causal"], a["bm"], a["bn"], None)
+                               a["dtype"], a["scale"], a["causal"], a["window"], a["bm"], a["bn"], None)
     if fn == "dkdv":
         return lib.fa_bwd_dkdv_rect(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dk"], a["dv"],
                                     a["bh"], a["nq"], a["nk"], a["d"], a["dtype"], a["scale"], a["causal"],
-                                    a["bm"], a["bn"], None)
+                                    a["window"], a["bm"], a["bn"], None)
     return lib.fa_bwd_dq_rect(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dq"], a["bh"],
-                              a["nq"], a["nk"], a["d"], a["dtype"], a["scale"], a["causal"], a["bm"], a["bn"],
-                              None)
+                              a["nq"], a["nk"], a["d"], a["dtype"], a["scale"], a["causal"], a["window"],
+                              a["bm"], a["bn"], None)
 
 
 def test_rect_lengths(lib):
@@ -174,6 +174,19 @@ def test_rect_lengths(lib):
         assert rect(lib, fn, nq=-1) == fa.FA_ERR_INVALID_ARG
         assert rect(lib, fn, nk=(1 << 24) + 1, causal=0) == fa.FA_ERR_UNSUPPORTED
         assert rect(lib, fn, q=A + 2) == fa.FA_ERR_MISALIGNED
+
+
+def test_rect_window_arguments(lib):
+    for fn in ("fwd", "dkdv", "dq"):
+        # a window is a positive key count, and only narrows causal attention
+        assert rect(lib, fn, window=-1) == fa.FA_ERR_INVALID_ARG
+        assert rect(lib, fn, window=16, causal=0) == fa.FA_ERR_INVALID_ARG
+        assert rect(lib, fn, window=-1, bh=0, q=0, k=0) == fa.FA_ERR_INVALID_ARG
+        # valid windows (any size, including wider than the keys) pass the
+        # argument checks and stop at the null q
+        for window in (1, 100, 128, 1 << 30, (1 << 31) - 1):
+            assert rect(lib, fn, window=window, q=0) == fa.FA_ERR_INVALID_ARG
+            assert rect(lib, fn, window=window, bh=0, q=0, k=0) == fa.FA_OK
 
 
 def test_empty_input_is_noop(lib):

@@ -26,13 +26,16 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def reference_attention(q, k, v, causal, scale):
+def reference_attention(q, k, v, causal, scale, window=0):
     """Causal masks are aligned to the end of the keys: query i sees keys
-    0 .. i + nk - nq."""
+    0 .. i + nk - nq, and with a window only the last `window` of them."""
     s = scale * torch.matmul(q, k.transpose(-1, -2))
     if causal:
         nq, nk = q.shape[-2], k.shape[-2]
-        s = s.masked_fill(torch.ones(nq, nk, dtype=torch.bool).triu(nk - nq + 1), float("-inf"))
+        hidden = torch.ones(nq, nk, dtype=torch.bool).triu(nk - nq + 1)
+        if window:
+            hidden |= torch.ones(nq, nk, dtype=torch.bool).tril(nk - nq - window)
+        s = s.masked_fill(hidden, float("-inf"))
     return torch.matmul(torch.softmax(s, dim=-1), v)
 
 
@@ -68,6 +71,32 @@ def test_matches_cpu_autograd(dtype, shape, nk, causal):
     assert err_o <= tol_o, err_o
     for name, a, b in (("dq", qd.grad, qc.grad), ("dk", kd.grad, kc.grad), ("dv", vd.grad, vc.grad)):
         assert a.dtype == dtype and a.shape == b.shape
+        err = _rel((a.cpu().double() - b).abs().max().item(), b)
+        assert err <= tol_g, (name, err)
+
+
+@pytest.mark.parametrize("dtype,shape,nk,window", [(torch.float32, (2, 2, 90, 32), 90, 13),
+                                                   (torch.bfloat16, (1, 2, 300, 128), 700, 200)])
+def test_window_matches_cpu_autograd(dtype, shape, nk, window):
+    _say(f"autograd window={window} dtype={dtype} q={shape} nk={nk}")
+    g = torch.Generator().manual_seed(8)
+    kshape = shape[:-2] + (nk, shape[-1])
+    q, w = (torch.randn(shape, generator=g, dtype=torch.float64) for _ in range(2))
+    k, v = (torch.randn(kshape, generator=g, dtype=torch.float64) for _ in range(2))
+    qd, kd, vd = (t.to(dtype).cuda().requires_grad_(True) for t in (q, k, v))
+    wd = w.to(dtype).cuda()
+    out = fa.flash_attention(qd, kd, vd, causal=True, window=window)
+    (out.float() * wd.float()).sum().backward()
+    torch.cuda.synchronize()
+
+    qc, kc, vc = (t.detach().cpu().double().requires_grad_(True) for t in (qd, kd, vd))
+    ref = reference_attention(qc, kc, vc, True, 1.0 / math.sqrt(shape[-1]), window)
+    (ref * wd.cpu().double()).sum().backward()
+
+    tol_o, tol_g = TOL[dtype]
+    err_o = (out.detach().cpu().double() - ref.detach()).abs().max().item()
+    assert err_o <= tol_o, err_o
+    for name, a, b in (("dq", qd.grad, qc.grad), ("dk", kd.grad, kc.grad), ("dv", vd.grad, vc.grad)):
         err = _rel((a.cpu().double() - b).abs().max().item(), b)
         assert err <= tol_g, (name, err)
 

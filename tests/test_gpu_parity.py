@@ -32,10 +32,12 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_gpu(arrays, dtype, causal, fwd_tiles=(0, 0), dkdv_tiles=(0, 0), dq_tiles=(0, 0), scale=None):
+def run_gpu(arrays, dtype, causal, fwd_tiles=(0, 0), dkdv_tiles=(0, 0), dq_tiles=(0, 0), scale=None,
+            window=0):
     q, k, v, do = cast_io(arrays, dtype, "cuda")
-    o, lse = fa.forward(q, k, v, causal, scale, *fwd_tiles)
-    dq, dk, dv, delta = fa.backward(q, k, v, o, do, lse, causal, scale, dkdv_tiles, dq_tiles)
+    o, lse = fa.forward(q, k, v, causal, scale, *fwd_tiles, window=window)
+    dq, dk, dv, delta = fa.backward(q, k, v, o, do, lse, causal, scale, dkdv_tiles, dq_tiles,
+                                    window=window)
     torch.cuda.synchronize()
     out = {name: to_f64(t) for name, t in
            dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta).items()}
@@ -48,7 +50,7 @@ def _rel(err, ref):
     return err / max(np.abs(ref).max(), 1.0 if np.abs(ref).max() == 0 else 0.0)
 
 
-def compare_full(g, dtype, causal, scale=None, label="", magnitude=1.0):
+def compare_full(g, dtype, causal, scale=None, label="", magnitude=1.0, window=0):
     """Whole-tensor comparison with the oracle; returns the error report.
 
     `magnitude` widens the O and L bounds for inputs whose scores are far
@@ -59,9 +61,10 @@ def compare_full(g, dtype, causal, scale=None, label="", magnitude=1.0):
     tol = dict(TOL[dtype])
     tol["o"] *= magnitude
     tol["lse"] *= magnitude
-    o_ref, l_ref = oracle.attention_forward(g["q"], g["k"], g["v"], scale=scale, causal=causal)
+    o_ref, l_ref = oracle.attention_forward(g["q"], g["k"], g["v"], scale=scale, causal=causal,
+                                            window=window)
     dq_ref, dk_ref, dv_ref, _ = oracle.attention_backward(g["q"], g["k"], g["v"], g["do"], scale=scale,
-                                                          causal=causal)
+                                                          causal=causal, window=window)
     # D from the GPU's own stored O (the identity the backward uses)
     d_ref = oracle.delta_from_output(g["o"], g["do"])
     rep = {
@@ -196,16 +199,16 @@ def test_determinism_bitwise():
 
 
 # --------------------------------------------------------------------------- full-size, sampled
-def sampled_check(w, causal, heads, rows, cols):
+def sampled_check(w, causal, heads, rows, cols, window=0):
     arrays = make_inputs(w.bh, w.n, w.d, seed=0)
-    g = run_gpu(arrays, w.dtype, causal)
+    g = run_gpu(arrays, w.dtype, causal, window=window)
     tol = TOL[w.dtype]
     for h in heads:
         q, k, v, do = (g[x][h] for x in ("q", "k", "v", "do"))
-        o_ref, l_ref = oracle.forward_rows(q, k, v, rows, causal=causal)
-        dq_ref, d_ref = oracle.dq_rows(q, k, v, do, rows, causal=causal)
-        stats = oracle.head_row_stats(q, k, v, do, causal=causal)
-        dk_ref, dv_ref = oracle.dkdv_cols(q, k, v, do, cols, causal=causal, stats=stats)
+        o_ref, l_ref = oracle.forward_rows(q, k, v, rows, causal=causal, window=window)
+        dq_ref, d_ref = oracle.dq_rows(q, k, v, do, rows, causal=causal, window=window)
+        stats = oracle.head_row_stats(q, k, v, do, causal=causal, window=window)
+        dk_ref, dv_ref = oracle.dkdv_cols(q, k, v, do, cols, causal=causal, stats=stats, window=window)
         # gradient scale from the whole head's GPU gradients (the reference max
         # over the sampled entries would understate it)
         rep = {
@@ -215,7 +218,8 @@ def sampled_check(w, causal, heads, rows, cols):
             "dk": np.abs(g["dk"][h][cols] - dk_ref).max() / np.abs(g["dk"][h]).max(),
             "dv": np.abs(g["dv"][h][cols] - dv_ref).max() / np.abs(g["dv"][h]).max(),
         }
-        _say(f"[{w.name} causal={causal} head={h}] " + " ".join(f"{a}={b:.2e}" for a, b in rep.items()))
+        _say(f"[{w.name} causal={causal} window={window} head={h}] " +
+             " ".join(f"{a}={b:.2e}" for a, b in rep.items()))
         assert rep["o"] <= tol["o"] and rep["lse"] <= tol["lse"], rep
         for name in ("dq", "dk", "dv"):
             assert rep[name] <= tol["grad"], (name, rep)
@@ -292,3 +296,90 @@ def test_rect_rejects_causal_with_more_queries():
     arrays = make_rect_inputs(1, 65, 64, 64, seed=33)
     with pytest.raises(fa.FAError):
         run_gpu(arrays, "bf16", True)
+
+
+# --------------------------------------------------------------------------- sliding window
+# Causal attention restricted to each query's `window` most recent keys
+# (window_attention_torch of "CS324 lecture 8, 03_online_softmax_and_flash.py").
+# The windows cross tile edges at every offset: 1 (the diagonal alone), sizes
+# below, at and above one tile, and windows wider than the sequence.
+@pytest.mark.parametrize("window", [1, 7, 16, 37, 100, 199])
+@pytest.mark.parametrize("tiles", [(16, 12), (64, 64), (32, 16)])
+def test_window_fp32(window, tiles):
+    arrays = make_inputs(2, 200, 32, seed=40)
+    g = run_gpu(arrays, "fp32", True, tiles, tiles, tiles, window=window)
+    compare_full(g, "fp32", True, label=f"fp32 window={window} n=200 tiles={tiles}", window=window)
+
+
+@pytest.mark.parametrize("nq,nk,window", [(37, 100, 5), (37, 100, 70), (64, 200, 33), (1, 64, 10)])
+def test_window_rect_fp32(nq, nk, window):
+    arrays = make_rect_inputs(2, nq, nk, 32, seed=41)
+    for tiles in ((16, 12), (64, 64)):
+        g = run_gpu(arrays, "fp32", True, tiles, tiles, tiles, window=window)
+        compare_full(g, "fp32", True, label=f"fp32 rect {nq}x{nk} window={window} tiles={tiles}",
+                     window=window)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window", [1, 37, 64, 100, 257, 700])
+@pytest.mark.parametrize("n", [333, 1000])
+def test_window_bf16(d, window, n):
+    arrays = make_inputs(2, n, d, seed=42)
+    g = run_gpu(arrays, "bf16", True, window=window)
+    compare_full(g, "bf16", True, label=f"bf16 d={d} n={n} window={window}", window=window)
+
+
+@pytest.mark.parametrize("fwd_tiles,dkdv_tiles", [((128, 64), (128, 128)), ((256, 64), (64, 128))])
+@pytest.mark.parametrize("window", [50, 300])
+def test_window_bf16_tilings(fwd_tiles, dkdv_tiles, window):
+    arrays = make_inputs(2, 1000, 128, seed=43)
+    g = run_gpu(arrays, "bf16", True, fwd_tiles, dkdv_tiles, window=window)
+    compare_full(g, "bf16", True, label=f"bf16 window={window} tiles={fwd_tiles},{dkdv_tiles}",
+                 window=window)
+
+
+@pytest.mark.parametrize("nq,nk,window", [(300, 1000, 128), (256, 4096, 1000), (1, 513, 100)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_rect_bf16(nq, nk, window, d):
+    arrays = make_rect_inputs(2, nq, nk, d, seed=44)
+    g = run_gpu(arrays, "bf16", True, window=window)
+    compare_full(g, "bf16", True, label=f"bf16 rect d={d} {nq}x{nk} window={window}", window=window)
+
+
+def test_window_one_is_the_diagonal():
+    """window = 1: each query sees only its own key, so P = 1 and O is that
+    key's value row exactly; L is the scaled diagonal score."""
+    arrays = make_inputs(2, 300, 128, seed=45)
+    g = run_gpu(arrays, "bf16", True, window=1)
+    assert np.array_equal(g["o"], g["v"])
+    diag = np.einsum("hnd,hnd->hn", g["q"], g["k"]) / math.sqrt(128)
+    assert np.abs(g["lse"] - diag).max() <= 1e-5 * max(1.0, np.abs(diag).max())
+    assert np.array_equal(g["dv"], g["do"])
+
+
+def test_window_covering_the_sequence_is_plain_causal():
+    """A window of at least nk keys hides nothing: bitwise the causal result."""
+    arrays = make_inputs(2, 500, 64, seed=46)
+    a = run_gpu(arrays, "bf16", True)
+    for window in (500, 501, 1 << 30):
+        b = run_gpu(arrays, "bf16", True, window=window)
+        for name in ("o", "lse", "dq", "dk", "dv"):
+            assert np.array_equal(a[name], b[name]), (window, name)
+
+
+def test_window_sampled_8192():
+    """BH = 32, N = 8192, d = 128, bf16, causal with a 1024-key window, at the
+    default tilings; sampled rows and columns against the oracle."""
+    w = WORKLOADS["headline_8192_d128"]
+    rng = np.random.default_rng(97)
+    rows = np.unique(np.concatenate([[0, 1, 1023, 1024, 1025, 4095, 8191], rng.integers(0, w.n, 16)]))
+    cols = np.unique(np.concatenate([[0, 1, 1024, 7167, 7168, 8191], rng.integers(0, w.n, 8)]))
+    sampled_check(w, True, heads=[3], rows=rows, cols=cols, window=1024)
+
+
+def test_window_rejects_bad_arguments():
+    arrays = make_inputs(1, 64, 64, seed=47)
+    with pytest.raises(fa.FAError):
+        run_gpu(arrays, "bf16", False, window=16)
+    with pytest.raises(fa.FAError):
+        run_gpu(arrays, "bf16", True, window=-1)
