@@ -43,6 +43,7 @@ class FAError(RuntimeError):
 
 
 _lib = None
+ABI_VERSION = 3   # FA_ABI_VERSION of include/fa.h that SIGNATURES describe
 
 
 def load_library(path: str = LIB_PATH):
@@ -59,6 +60,9 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_char_p if name == "fa_status_str" else ctypes.c_int
+    if lib.fa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI {lib.fa_abi_version()}, the binding expects {ABI_VERSION}: "
+                           "rebuild the HIP library")
     _lib = lib
     return lib
 

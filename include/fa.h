@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     for code in range(5):
         assert fa.fa_status_str(code)
     assert fa.fa_status_str(99) == "unknown status"
