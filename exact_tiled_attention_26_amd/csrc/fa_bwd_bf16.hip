@@ -49,7 +49,8 @@ __device__ __forceinline__ void rows_load_async(float* lds, const float* src, in
 // of the key sequence (query i sees keys 0 .. i + nk - nq), and a window > 0
 // hides keys at or below i + nk - nq - window.
 // RAGGED: nq may not be a multiple of BR (the last query tile needs the mask).
-template <int D, int KW, int NW, int BR, bool CAUSAL, bool RAGGED>
+// BAND: causal with a window (0 < window < nk).
+template <int D, int KW, int NW, int BR, bool CAUSAL, bool RAGGED, bool BAND>
 __global__ __launch_bounds__(NW * 64, 1)
 void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -76,7 +77,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int k0 = kt * BC;
   const int k0w = k0 + wave * KW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
-  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
+  const int lo = BAND ? off - window : 0;   // with a window: only keys above i + lo
   const size_t hoffq = (size_t)head * nq * D, hoffk = (size_t)head * nk * D;
   const __bf16* Qh = Q + hoffq;
   const __bf16* dOh = dO + hoffq;
@@ -86,7 +87,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int ntq = (nq + BR - 1) / BR;
   const int it0 = CAUSAL ? max(0, k0 - off) / BR : 0;   // earlier query rows see none of these keys
   // later rows see none of them either once the window has moved past them
-  const int it1 = CAUSAL ? min(ntq, max(0, k0 + BC - 2 - lo) / BR + 1) : ntq;
+  const int it1 = BAND ? min(ntq, max(0, k0 + BC - 2 - lo) / BR + 1) : ntq;
   // compiler-visible copies: measured faster than the hidden form here
   const AsyncTileCopy<D, BR, NW, false> copier(wave, lane);
   auto issue_tile = [&](__bf16* qd, __bf16* od, float* ld, float* dd, int i0) __attribute__((always_inline)) {
@@ -182,7 +183,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         const int llim = q + lo - k0w - l16;   // key 16kb + .. hidden from below iff 16kb <= llim
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          if (16 * kb > lim || (CAUSAL && 16 * kb <= llim)) {
+          if (16 * kb > lim || (BAND && 16 * kb <= llim)) {
             e.pv[h][kb][i] = 0.f;
             e.dsv[h][kb][i] = 0.f;
           }
@@ -310,13 +311,13 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                        __bf16* qn, __bf16* on, float* ln, float* dn, int it) __attribute__((always_inline)) {
     const int i0 = it * BR;
     if (it + 1 < it1) issue_tile(qn, on, ln, dn, i0 + BR);
-    const bool active = !CAUSAL || (i0 + BR - 1 + off >= k0w && i0 + lo < k0w + KW - 1);
+    const bool active = !CAUSAL || (i0 + BR - 1 + off >= k0w && (!BAND || i0 + lo < k0w + KW - 1));
     if (active) {
       // only tiles crossing the diagonal, the window's edge or the end of the
       // sequence are masked; they run a separate copy so that the others carry
       // no mask arithmetic
       if ((CAUSAL || RAGGED) &&
-          ((CAUSAL && (i0 + off < k0w + KW - 1 || i0 + BR - 1 + lo >= k0w)) || (i0 + BR > nq))) {
+          ((CAUSAL && i0 + off < k0w + KW - 1) || (BAND && i0 + BR - 1 + lo >= k0w) || (i0 + BR > nq))) {
         run_tile(qt, ot, lt, dt, i0, std::true_type{});
       } else {
         run_tile(qt, ot, lt, dt, i0, std::false_type{});
@@ -352,7 +353,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   }
 }
 
-template <int D, int QW, int NW, int BC, bool CAUSAL>
+template <int D, int QW, int NW, int BC, bool CAUSAL, bool BAND>
 __global__ __launch_bounds__(NW * 64, 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -378,13 +379,13 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
-  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
+  const int lo = BAND ? off - window : 0;   // with a window: only keys above i + lo
   const size_t hoffq = (size_t)head * nq * D;
   const __bf16* Kh = K + (size_t)head * nk * D;
   const __bf16* Vh = V + (size_t)head * nk * D;
 
   const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
-  const int jt0 = max(0, q0 + lo + 1) / BC;   // first key tile a row of the workgroup can see
+  const int jt0 = BAND ? max(0, q0 + lo + 1) / BC : 0;   // first key tile a row of the workgroup can see
   const int ntk = (kend + BC - 1) / BC;
   // compiler-visible copies: measured faster than the hidden form here
   const AsyncTileCopy<D, BC, NW, false> copier(wave, lane);
@@ -428,7 +429,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       copier.issue(kn, Kh + (size_t)(j0 + BC) * D, nk - j0 - BC);
       copier.issue(vn, Vh + (size_t)(j0 + BC) * D, nk - j0 - BC);
     }
-    const bool active = !CAUSAL || (j0 <= q0w + QW - 1 + off && j0 + BC - 1 > q0w + lo);
+    const bool active = !CAUSAL || (j0 <= q0w + QW - 1 + off && (!BAND || j0 + BC - 1 > q0w + lo));
     if (active) {
       // S^T = K Q^T, dP^T = V dO^T: lane holds key 16kb + 4g + i, query 16qb + l16
       f32x4 s[NKB][NQB], dp[NKB][NQB];
@@ -465,7 +466,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool need_mask = (CAUSAL && (j0 + BC - 1 > q0w + off || j0 <= q0w + QW - 1 + lo)) ||
+      const bool need_mask = (CAUSAL && j0 + BC - 1 > q0w + off) || (BAND && j0 <= q0w + QW - 1 + lo) ||
                              (j0 + BC > nk);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
@@ -489,7 +490,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (16 * kb + i > lim || (CAUSAL && 16 * kb + i <= llim)) dp[kb][qb][i] = 0.f;
+              if (16 * kb + i > lim || (BAND && 16 * kb + i <= llim)) dp[kb][qb][i] = 0.f;
         }
       }
       // dQ^T += K^T dS^T (Eq 18, scale applied at the end)
@@ -555,8 +556,9 @@ static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, 
   // the non-causal kernel keeps its masked copy even when nq is a multiple of
   // BR: the uniform branch around it splits the tile into scheduling regions
   // small enough to stay within the register file
-  auto kern = causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true>
-                     : dkdv_bf16_kernel<D, KW, NW, BR, false, true>;
+  auto kern = (causal && window > 0) ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, true>
+             : causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, false>
+                      : dkdv_bf16_kernel<D, KW, NW, BR, false, true, false>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                      (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, bh, nq, nk, window, scale,
                      sl2);
@@ -572,15 +574,11 @@ static hipError_t launch_dq_inst(const void* q, const void* k, const void* v, co
   const int ntq = (nq + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
-  if (causal) {
-    hipLaunchKernelGGL((dq_bf16_kernel<D, QW, NW, BC, true>), grid, block, 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dq, bh, nq, nk, window, scale, sl2);
-  } else {
-    hipLaunchKernelGGL((dq_bf16_kernel<D, QW, NW, BC, false>), grid, block, 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       lse, delta, (__bf16*)dq, bh, nq, nk, window, scale, sl2);
-  }
+  auto kern = (causal && window > 0) ? dq_bf16_kernel<D, QW, NW, BC, true, true>
+             : causal ? dq_bf16_kernel<D, QW, NW, BC, true, false>
+                      : dq_bf16_kernel<D, QW, NW, BC, false, false>;
+  hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                     (const __bf16*)dO, lse, delta, (__bf16*)dq, bh, nq, nk, window, scale, sl2);
   return hipGetLastError();
 }
 

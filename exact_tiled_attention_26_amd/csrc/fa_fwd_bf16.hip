@@ -44,7 +44,8 @@ constexpr int kFwdBuffers = 2;   // LDS buffers per operand (copy distance NBUF 
 // of the key sequence (query i sees keys 0 .. i + nk - nq), and a window > 0
 // hides keys at or below i + nk - nq - window.
 // RAGGED: nk may not be a multiple of BC (the last key tile needs the mask).
-template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED, int NBUF>
+// BAND: causal with a window (0 < window < nk).
+template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED, bool BAND, int NBUF>
 __global__ __launch_bounds__(NW * 64, 2)
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -62,6 +63,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   static_assert(US == UP, "the two products of a tile are interleaved step by step");
   static_assert(NKS == 2, "probabilities are produced in two halves, one per PV half");
   static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
+  static_assert(!BAND || CAUSAL, "a window narrows causal attention");
 
   // NBUF LDS buffers per operand; K runs one tile ahead of V, and every copy
   // is issued NBUF - 1 steps before its data is used
@@ -77,17 +79,19 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
-  const int lo = window_lo(CAUSAL, off, window);   // ... and only keys above i + lo
+  const int lo = BAND ? off - window : 0;   // with a window: only keys above i + lo
   const __bf16* Qh = Q + (size_t)head * nq * D;
   const __bf16* Kh = K + (size_t)head * nk * D;
   const __bf16* Vh = V + (size_t)head * nk * D;
 
   const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;   // keys this workgroup can see
   const int ntk = (kend + BC - 1) / BC;
-  const int jt0 = max(0, q0 + lo + 1) / BC;   // first key tile a row of the workgroup can see
-  // last key tile with a key that one of this wave's rows can see
+  // first key tile a row of the workgroup can see
+  const int jt0 = BAND ? max(0, q0 + lo + 1) / BC : 0;
+  // first and last key tiles with a key that one of this wave's rows can see
   // (dz: see divergent_zero)
   const int dz = divergent_zero();
+  const int first = BAND ? max(jt0, (q0w + lo + 1) / BC) : 0;
   const int last = CAUSAL ? min(ntk - 1, (q0w + QW - 1 + off) / BC) : ntk - 1 + dz;
   const AsyncTileCopy<D, BC, NW> copier(wave, lane);
   // buffers are indexed by the tile's position t - jt0 in the loop
@@ -132,7 +136,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // does key tile j need the in-tile mask for this wave?
   auto tile_masked = [&](int j) __attribute__((always_inline)) {
-    return (CAUSAL && (j * BC + BC - 1 > q0w + off || j * BC <= q0w + QW - 1 + lo)) ||
+    return (CAUSAL && j * BC + BC - 1 > q0w + off) || (BAND && j * BC <= q0w + QW - 1 + lo) ||
            (RAGGED && j * BC + BC > nk + dz);
   };
   // in-tile mask: key j0 + 16kb + 4g + i is visible iff llim < 16kb + i <= lim
@@ -142,7 +146,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int llim = q0w + 16 * qb + l16 + lo - j0 - 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (16 * kb + i > lim || (CAUSAL && 16 * kb + i <= llim)) s[kb][qb][i] = kNegInf;
+      if (16 * kb + i > lim || (BAND && 16 * kb + i <= llim)) s[kb][qb][i] = kNegInf;
   };
   // scaled max (base 2) of one query block over this lane's 16 keys of the
   // tile; the other three lanes of the query hold the rest of the row
@@ -189,7 +193,23 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   };
 
-  // prologue: scores of tile 0 and the first exponent base
+  // scores of key tile j (keys in kt), masked when needed, and the exponent
+  // base they call for
+  auto scores_only = [&](f32x4 (&s)[NKB][NQB], const __bf16* kt, int j) __attribute__((always_inline)) {
+    s_gemm_plain(s, kt);
+    if (tile_masked(j)) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) mask_item(s, j * BC, qb, kb);
+    }
+    float mx[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) mx[qb] = row_max(s, qb);
+    update_base(mx);
+  };
+
+  // prologue: scores of the first key tile and the first exponent base
   async_copy_wait();
   // copies that step 0 waits for when the distance is two steps
   if constexpr (NBUF == 3) {
@@ -197,19 +217,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (jt0 + 2 < ntk) copier.issue(k_lds[2], Kh + (size_t)(jt0 + 2) * BC * D, nk - (jt0 + 2) * BC);
   }
   __syncthreads();
-  s_gemm_plain(sa, k_lds[0]);
-  if (tile_masked(jt0)) {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mask_item(sa, jt0 * BC, qb, kb);
-  }
-  {
-    float mx[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) mx[qb] = row_max(sa, qb);
-    update_base(mx);
-  }
+  // (a wave whose band starts later computes its first scores in the step before)
+  if (!BAND || first == jt0) scores_only(sa, k_lds[0], jt0);
   __syncthreads();   // every wave is done with K(0) before its buffer is refilled
 
   // One pipelined step: probabilities and PV of tile t (scores in sc, values
@@ -313,8 +322,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // Step t: K(t+1) and V(t) are resident.  Copy K(t+NBUF) and V(t+NBUF-1)
   // into the buffers that step t-1 finished with, run the pipelined body when
-  // this wave has rows that see tile t, then wait for the copies that step
-  // t+1 needs and synchronise.
+  // this wave has rows that see tile t (with a window, only the scores of
+  // tile t+1 in the step before the wave's first tile), then wait for the
+  // copies that step t+1 needs and synchronise.
   constexpr int PER = AsyncTileCopy<D, BC, NW>::PER_WAVE;   // copy instructions per tile and wave
   auto step = [&](f32x4 (&sc)[NKB][NQB], f32x4 (&sn)[NKB][NQB], int t) __attribute__((always_inline)) {
     const int r = t - jt0;
@@ -322,7 +332,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const bool ck = t + NBUF < ntk, cv = t + NBUF - 1 < ntk;
     if (cv) copier.issue(v_lds[bl], Vh + (size_t)(t + NBUF - 1) * BC * D, nk - (t + NBUF - 1) * BC);
     if (ck) copier.issue(k_lds[b0], Kh + (size_t)(t + NBUF) * BC * D, nk - (t + NBUF) * BC);
-    if (t <= last) {
+    if (t <= last && (!BAND || t >= first)) {
       const __bf16* kn = k_lds[b1];
       const __bf16* vt = v_lds[b0];
       if (t + 1 <= last) {
@@ -334,6 +344,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       } else {
         body(sc, sn, kn, vt, t, std::false_type{}, std::false_type{});
       }
+    } else if constexpr (BAND) {
+      if (t + 1 == first && first <= last) scores_only(sn, k_lds[b1], t + 1);
     }
     if constexpr (NBUF == 3) {
       if (ck) async_copy_wait_allbut<2 * PER>();
@@ -379,9 +391,10 @@ static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, v
   const int ntq = (nq + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
-  auto kern = causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true, kFwdBuffers>
-            : (nk % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, kFwdBuffers>
-                       : fwd_bf16_kernel<D, QW, NW, BC, false, false, kFwdBuffers>;
+  auto kern = (causal && window > 0) ? fwd_bf16_kernel<D, QW, NW, BC, true, true, true, kFwdBuffers>
+            : causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true, false, kFwdBuffers>
+            : (nk % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, false, kFwdBuffers>
+                       : fwd_bf16_kernel<D, QW, NW, BC, false, false, false, kFwdBuffers>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                      (__bf16*)o, lse, bh, nq, nk, window, sl2);
   return hipGetLastError();
