@@ -50,7 +50,8 @@ def kernel_flops(bh, n, d, causal, window=0):
     must perform over the needed score pairs): fwd S and PV (4 N^2 d); dK/dV
     kernel S, dP, dV, dK (8 N^2 d); dQ kernel S, dP, dQ (6 N^2 d)."""
     u = 2.0 * score_pairs(n, causal, window) * d * bh
-    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u}
+    # the single-kernel backward runs S, dP, dV, dK and dQ once each
+    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd_fused": 5 * u}
 
 
 def kernel_bytes(bh, n, d, elt):
@@ -58,7 +59,9 @@ def kernel_bytes(bh, n, d, elt):
     written once)."""
     t = bh * n * d * elt
     r = bh * n * 4
-    return {"fwd": 4 * t + r, "preprocess": 2 * t + r, "dkdv": 6 * t + 2 * r, "dq": 5 * t + 2 * r}
+    # the single-kernel backward also clears, accumulates and rounds an fp32 dQ
+    return {"fwd": 4 * t + r, "preprocess": 2 * t + r, "dkdv": 6 * t + 2 * r, "dq": 5 * t + 2 * r,
+            "bwd_fused": 8 * t + 2 * r + 3 * bh * n * d * 4}
 
 
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "attention_kernels_headline_8192_d128_causal_bf16.md")
@@ -168,6 +171,9 @@ def main():
     ap.add_argument("--non-causal", action="store_true")
     ap.add_argument("--window", type=int, default=0,
                     help="causal sliding window of this many keys (0: none)")
+    ap.add_argument("--fused-bwd", action="store_true",
+                    help="time the single-kernel backward (fa_bwd_fused, atomic dQ) instead of "
+                         "fa_bwd_dkdv + fa_bwd_dq")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--fwd-tiles", default="0,0")
@@ -225,7 +231,11 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    names = ("fwd", "preprocess", "dkdv", "dq")
+    names = ("fwd", "preprocess", "bwd_fused") if args.fused_bwd else ("fwd", "preprocess", "dkdv", "dq")
+    ws = None
+    if args.fused_bwd:
+        nbytes = fa.fa_bwd_fused_workspace_bytes(bh, n, d, fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda") if nbytes else None
 
     if window:
         def fwd_call():
@@ -247,28 +257,26 @@ def main():
         def dq_call():
             fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr)
 
+    def fused_call():
+        fa.fa_bwd_fused(q, k, v, do, lse, delta, dq, dk, dv, ws, causal, None, *kt, stream=sptr, window=window)
+
+    calls = [fwd_call, lambda: fa.fa_bwd_preprocess(o, do, delta, stream=sptr)]
+    calls += [fused_call] if args.fused_bwd else [dkdv_call, dq_call]
+
     def step(ev=None):
+        for j, call in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            call()
         if ev is not None:
-            ev[0].record(stream)
-        fwd_call()
-        if ev is not None:
-            ev[1].record(stream)
-        fa.fa_bwd_preprocess(o, do, delta, stream=sptr)
-        if ev is not None:
-            ev[2].record(stream)
-        dkdv_call()
-        if ev is not None:
-            ev[3].record(stream)
-        dq_call()
-        if ev is not None:
-            ev[4].record(stream)
+            ev[len(calls)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -281,7 +289,7 @@ def main():
     for ev in events:
         for j, nm in enumerate(names):
             per_kernel[nm].append(ev[j].elapsed_time(ev[j + 1]))
-        step_ms.append(ev[0].elapsed_time(ev[4]))
+        step_ms.append(ev[0].elapsed_time(ev[len(names)]))
     avg = {nm: sum(x) / len(x) for nm, x in per_kernel.items()}
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = sum(step_ms) / len(step_ms)
@@ -290,12 +298,12 @@ def main():
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     tflops = (fwd_fl + bwd_fl) / (ms_per_step * 1e-3) / 1e12
     fwd_tf = fwd_fl / (avg["fwd"] * 1e-3) / 1e12
-    bwd_ms = avg["preprocess"] + avg["dkdv"] + avg["dq"]
+    bwd_ms = sum(avg[nm] for nm in names if nm != "fwd")
     bwd_tf = bwd_fl / (bwd_ms * 1e-3) / 1e12
 
     kfl = kernel_flops(bh, n, d, causal, window)
     kby = kernel_bytes(bh, n, d, elt)
-    dom = max(("fwd", "dkdv", "dq"), key=lambda nm: avg[nm])
+    dom = max((nm for nm in names if nm != "preprocess"), key=lambda nm: avg[nm])
     achieved = kfl[dom] / (avg[dom] * 1e-3) / 1e12
     roofline = {
         "kernel": dom,
@@ -306,7 +314,7 @@ def main():
         "frac": round(achieved / peak, 4),
         "traffic": (measured_traffic(dom)
                     if (w.name == "headline_8192_d128" and causal and not window and ft == (0, 0)
-                        and kt == (0, 0) and qt == (0, 0)) else None),
+                        and kt == (0, 0) and qt == (0, 0) and not args.fused_bwd) else None),
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
         "avg_launch_ms": round(avg[dom], 4),
         "algorithmic_flops_per_launch": kfl[dom],
@@ -339,7 +347,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: seeded N(0,1) Q, K, V, dO (numpy default_rng(0), cast to bf16)",
         "config": {"workload": w.name, "batch_heads": bh, "seq_len": n, "head_dim": d,
-                   "causal": causal, "window": window, "tiles": {"fwd": list(ft), "dkdv": list(kt), "dq": list(qt)}},
+                   "causal": causal, "window": window,
+                   "backward": "fused (fa_bwd_fused)" if args.fused_bwd else "two-kernel", "tiles": {"fwd": list(ft), "dkdv": list(kt), "dq": list(qt)}},
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
         "fwd_tflops": round(fwd_tf, 1),
         "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),

@@ -15,12 +15,16 @@ from ._lib import (  # noqa: F401
     FA_OK,
     KERNEL_DKDV,
     KERNEL_DQ,
+    KERNEL_FUSED,
     KERNEL_FWD,
     LIB_PATH,
     SIGNATURES,
     FAError,
     backward,
+    backward_fused,
     fa_abi_version,
+    fa_bwd_fused,
+    fa_bwd_fused_workspace_bytes,
     fa_bwd_dkdv,
     fa_bwd_dq,
     fa_bwd_dq_rect,

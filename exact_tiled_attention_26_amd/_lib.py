@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_F32, FA_BF16 = 0, 1
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_HIP = range(5)
-KERNEL_FWD, KERNEL_DKDV, KERNEL_DQ = 0, 1, 2
+KERNEL_FWD, KERNEL_DKDV, KERNEL_DQ, KERNEL_FUSED = 0, 1, 2, 3
 
 # (name, argtypes) for every function include/fa.h declares
 _P, _I, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -30,6 +30,8 @@ SIGNATURES = {
     "fa_fwd_rect": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
     "fa_bwd_dkdv_rect": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
     "fa_bwd_dq_rect": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
+    "fa_bwd_fused": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
+    "fa_bwd_fused_workspace_bytes": [_I, _I, _I, _I],
     "fa_default_tiles": [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "fa_status_str": [_I],
     "fa_abi_version": [],
@@ -43,7 +45,7 @@ class FAError(RuntimeError):
 
 
 _lib = None
-ABI_VERSION = 3   # FA_ABI_VERSION of include/fa.h that SIGNATURES describe
+ABI_VERSION = 4   # FA_ABI_VERSION of include/fa.h that SIGNATURES describe
 
 
 def load_library(path: str = LIB_PATH):
@@ -59,7 +61,8 @@ def load_library(path: str = LIB_PATH):
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name == "fa_status_str" else ctypes.c_int
+        fn.restype = {"fa_status_str": ctypes.c_char_p,
+                      "fa_bwd_fused_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
     if lib.fa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path} has ABI {lib.fa_abi_version()}, the binding expects {ABI_VERSION}: "
                            "rebuild the HIP library")
@@ -239,6 +242,32 @@ def fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, causal: bool, scale: float | Non
     _check("fa_bwd_dq_rect", st)
 
 
+def fa_bwd_fused_workspace_bytes(bh: int, nq: int, d: int, dtype: int) -> int:
+    return int(load_library().fa_bwd_fused_workspace_bytes(int(bh), int(nq), int(d), int(dtype)))
+
+
+def fa_bwd_fused(q, k, v, dO, lse, delta, dq, dk, dv, workspace, causal: bool, scale: float | None = None,
+                 block_m: int = 0, block_n: int = 0, stream=None, window: int = 0):
+    """Single-kernel backward: dK, dV and dQ (atomic adds) for q, dO
+    [bh, nq, d] against k, v [bh, nk, d].  bf16 needs `workspace`, a float32
+    device tensor of fa_bwd_fused_workspace_bytes bytes; float32 takes None."""
+    import torch
+    bh, nq, d = _shape3(q)
+    nk = _kv_shape(q, k)
+    _check_io(q, [("q", q, "io"), ("k", k, "kv"), ("v", v, "kv"), ("dO", dO, "io"), ("lse", lse, "row"),
+                  ("delta", delta, "row"), ("dq", dq, "io"), ("dk", dk, "kv"), ("dv", dv, "kv")], None, kref=k)
+    if workspace is not None:
+        _require(workspace.is_cuda and workspace.is_contiguous() and workspace.dtype == torch.float32,
+                 "workspace must be a contiguous float32 device tensor")
+        _require(workspace.numel() * 4 >= fa_bwd_fused_workspace_bytes(bh, nq, d, _dtype_code(q)),
+                 "workspace is smaller than fa_bwd_fused_workspace_bytes")
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), _ptr(workspace), bh, nq, nk, d, _dtype_code(q), scale,
+                                     int(bool(causal)), int(window), int(block_m), int(block_n), _stream(stream))
+    _check("fa_bwd_fused", st)
+
+
 # ------------------------------------------------------------------ allocating helpers
 def forward(q, k, v, causal: bool, scale=None, block_m=0, block_n=0, stream=None, window=0):
     """Allocate O and L with torch and run fa_fwd (fa_fwd_rect when k has a
@@ -269,4 +298,18 @@ def backward(q, k, v, o, dO, lse, causal: bool, scale=None, tiles_dkdv=(0, 0), t
                          window=window)
         fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, causal, scale, *tiles_dq, stream=stream,
                        window=window)
+    return dq, dk, dv, delta
+
+
+def backward_fused(q, k, v, o, dO, lse, causal: bool, scale=None, tiles=(0, 0), stream=None, window=0):
+    """Allocate D, dQ, dK, dV (and the bf16 workspace) with torch and run
+    fa_bwd_preprocess then fa_bwd_fused on one stream; returns
+    (dq, dk, dv, delta)."""
+    import torch
+    delta = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = fa_bwd_fused_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], _dtype_code(q))
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device) if nbytes else None
+    fa_bwd_preprocess(o, dO, delta, stream)
+    fa_bwd_fused(q, k, v, dO, lse, delta, dq, dk, dv, ws, causal, scale, *tiles, stream=stream, window=window)
     return dq, dk, dv, delta

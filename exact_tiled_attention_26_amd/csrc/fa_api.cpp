@@ -14,7 +14,7 @@ constexpr int kMaxN = 1 << 24;          // keeps row * D offsets and grids in ra
 constexpr int kMaxBH = 1 << 20;
 constexpr size_t kLdsBudget = 160 * 1024;
 
-enum Kernel { kFwd = 0, kDkdv = 1, kDq = 2 };
+enum Kernel { kFwd = 0, kDkdv = 1, kDq = 2, kFused = 3 };
 
 struct Tiles { int bm, bn; };
 
@@ -25,6 +25,7 @@ constexpr Bf16Tiling kBf16Tilings[] = {
     {kFwd, 64, 128, 64},   {kFwd, 64, 256, 64},
     {kDkdv, 128, 64, 128}, {kDkdv, 128, 128, 128}, {kDkdv, 64, 64, 128},
     {kDq, 128, 128, 64},   {kDq, 64, 128, 64},
+    {kFused, 128, 64, 128}, {kFused, 64, 64, 128},
 };
 
 constexpr Tiles kF32Default = {64, 64};
@@ -129,7 +130,7 @@ const char* fa_status_str(fa_status s) {
 fa_status fa_default_tiles(fa_dtype dtype, int d, int kernel, int* block_m, int* block_n) {
   if (block_m == nullptr || block_n == nullptr) return FA_ERR_INVALID_ARG;
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
-  if (kernel < 0 || kernel > 2) return FA_ERR_INVALID_ARG;
+  if (kernel < 0 || kernel > 3) return FA_ERR_INVALID_ARG;
   int bm = 0, bn = 0;
   const fa_status s = resolve_tiles(dtype, kernel, d, bm, bn);
   if (s != FA_OK) return s;
@@ -231,6 +232,41 @@ fa_status fa_bwd_dq_rect(const void* q, const void* k, const void* v, const void
   return from_hip(fa::launch_dq_f32((const float*)q, (const float*)k, (const float*)v,
                                     (const float*)dO, lse, delta, (float*)dq, bh, nq, nk, d,
                                     scale, causal != 0, window, block_m, block_n, st));
+}
+
+size_t fa_bwd_fused_workspace_bytes(int bh, int nq, int d, fa_dtype dtype) {
+  if (dtype != FA_BF16 || bh <= 0 || nq <= 0 || d <= 0) return 0;
+  return (size_t)bh * (size_t)nq * (size_t)d * sizeof(float);
+}
+
+fa_status fa_bwd_fused(const void* q, const void* k, const void* v, const void* dO,
+                       const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                       float* workspace, int bh, int nq, int nk, int d, fa_dtype dtype,
+                       float scale, int causal, int window, int block_m, int block_n,
+                       void* stream) {
+  fa_status s = check_common(bh, nq, nk, d, dtype);
+  if (s != FA_OK) return s;
+  if ((s = check_scale(scale)) != FA_OK) return s;
+  if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
+  if ((s = resolve_tiles(dtype, kFused, d, block_m, block_n)) != FA_OK) return s;
+  bool empty = false;
+  if ((s = check_lengths(bh, nq, nk, causal, window, empty)) != FA_OK || empty) return s;
+  if ((s = check_grid(bh, nk, block_n)) != FA_OK) return s;
+  if ((s = check_ptrs(q, k, v, dO, lse, delta, dq, dk, dv)) != FA_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == FA_BF16) {
+    if ((s = check_ptrs(workspace)) != FA_OK) return s;
+    if (any_equal({dq, dk, dv, workspace}, {q, k, v, dO, lse, delta, dq, dk, dv, workspace}))
+      return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_bwd_fused_bf16(q, k, v, dO, lse, delta, dq, dk, dv, workspace, bh, nq,
+                                              nk, d, scale, causal != 0, window, block_m, block_n,
+                                              st));
+  }
+  if (any_equal({dq, dk, dv}, {q, k, v, dO, lse, delta, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  return from_hip(fa::launch_bwd_fused_f32((const float*)q, (const float*)k, (const float*)v,
+                                           (const float*)dO, lse, delta, (float*)dq, (float*)dk,
+                                           (float*)dv, bh, nq, nk, d, scale, causal != 0, window,
+                                           block_m, block_n, st));
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,

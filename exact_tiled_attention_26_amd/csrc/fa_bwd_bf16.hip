@@ -23,6 +23,7 @@
 // * Causal mode visits only the tiles that hold a visible (query, key) pair
 //   and masks only tiles crossing the diagonal.  Workgroups are ordered with
 //   the heaviest tiles first.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -50,24 +51,34 @@ __device__ __forceinline__ void rows_load_async(float* lds, const float* src, in
 // hides keys at or below i + nk - nq - window.
 // RAGGED: nq may not be a multiple of BR (the last query tile needs the mask).
 // BAND: causal with a window (0 < window < nk).
-template <int D, int KW, int NW, int BR, bool CAUSAL, bool RAGGED, bool BAND>
+// FUSED: also accumulate dQ (unscaled, fp32) into dQacc with atomic adds,
+// the single-kernel backward: after each 32-query step the waves put dS in
+// LDS and wave w adds dS K for head-dim columns [w D/NW, (w+1) D/NW) over
+// the workgroup's BC keys; K stays in LDS for the whole kernel.
+template <int D, int KW, int NW, int BR, bool CAUSAL, bool RAGGED, bool BAND, bool FUSED = false>
 __global__ __launch_bounds__(NW * 64, 1)
 void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                      __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+                      __bf16* __restrict__ dK, __bf16* __restrict__ dV, float* __restrict__ dQacc,
                       int bh, int nq, int nk, int window, float scale, float scale_log2) {
   constexpr int BC = KW * NW;
   constexpr int NKB = KW / 16;   // 16-key blocks per wave
   constexpr int NDS = D / 32;
   constexpr int NDB = D / 16;
   constexpr int NQS = BR / 32;   // 32-query steps per query tile
+  constexpr int DW = D / NW;     // fused dQ: head-dim columns per wave
   static_assert(NW >= 2, "two waves stage the row values");
+  static_assert(!FUSED || (DW % 16 == 0 && BC % 32 == 0), "fused dQ split");
 
   __shared__ __bf16 q_lds0[BR * D], q_lds1[BR * D];
   __shared__ __bf16 o_lds0[BR * D], o_lds1[BR * D];
   __shared__ float l_lds0[BR], l_lds1[BR];
   __shared__ float d_lds0[BR], d_lds1[BR];
+  // fused dQ: the workgroup's K rows (swizzled like the Q tiles) and dS of
+  // the last two 32-query steps, stored [key][query]
+  __shared__ __bf16 kt_lds[FUSED ? BC * D : 8];
+  __shared__ __bf16 ds_lds[FUSED ? 2 * BC * 32 : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -96,6 +107,10 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     if (wave == 0) rows_load_async<BR>(ld, Lh, i0, nq, lane);
     if (wave == 1) rows_load_async<BR>(dd, Dh, i0, nq, lane);
   };
+  if constexpr (FUSED) {
+    const AsyncTileCopy<D, BC, NW, false> kcopier(wave, lane);
+    kcopier.issue(kt_lds, K + hoffk + (size_t)k0 * D, nk - k0);
+  }
   issue_tile(q_lds0, o_lds0, l_lds0, d_lds0, it0 * BR);
 
   // K and V rows of this wave as B operands: lane holds row k0w + 16kb + l16,
@@ -130,6 +145,76 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const TrReader<D> tr(l16, g);
   async_copy_wait();
   __syncthreads();
+  if constexpr (FUSED) {
+    // K rows past nk were copied from row nk - 1: clear them so that those
+    // keys add nothing to dQ
+    if (k0 + BC > nk) {
+      for (int e = tid; e < (k0 + BC - nk) * (D / 8); e += NW * 64)
+        *reinterpret_cast<bf16x8*>(kt_lds + (size_t)(nk - k0 + e / (D / 8)) * D + 8 * (e % (D / 8))) = bf16x8{};
+      __syncthreads();
+    }
+  }
+
+  // Fused dQ of one 32-query step (queries i0 + 32t ..): dS is stored
+  // [key][query] with rows of 32 queries; the 16-query halves of a row swap
+  // when bit 2 of the key is set, so the transposed reads below are free of
+  // bank conflicts.  dQ[q][d] += sum over the BC keys of dS[q][key] K[key][d]
+  // with A = dS (read transposed from ds_lds) and B = K (read transposed
+  // from kt_lds); the lane then holds query 16qb + 4g + i, column
+  // w DW + 16nb + l16, added to dQacc with one atomic per value.
+  auto ds_off = [&](int row, int col) __attribute__((always_inline)) {
+    return row * 32 + (col ^ (16 * ((row >> 2) & 1)));
+  };
+  auto dq_step = [&](const bf16x8 (&sb)[NKB], int i0, int t, __bf16* dsl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int row = wave * KW + 16 * kb + l16;
+      *reinterpret_cast<bf16x4*>(dsl + ds_off(row, 4 * g)) = __builtin_shufflevector(sb[kb], sb[kb], 0, 1, 2, 3);
+      *reinterpret_cast<bf16x4*>(dsl + ds_off(row, 16 + 4 * g)) = __builtin_shufflevector(sb[kb], sb[kb], 4, 5, 6, 7);
+    }
+    __syncthreads();
+    constexpr int NB = DW / 16;
+    f32x4 acc[2][NB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[qb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int trow = 4 * g + (l16 >> 2);          // transposed read: row in a 16-row block
+#pragma unroll
+    for (int kk = 0; kk < BC / 32; ++kk) {
+      bf16x8 a[2], b[NB];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int c = 16 * qb + 4 * (l16 & 3);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(dsl + ds_off(32 * kk + trow, c)));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(dsl + ds_off(32 * kk + 16 + trow, c)));
+        a[qb] = cat(lo, hi);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int db = wave * NB + nb;
+        b[nb] = cat(tr.read(kt_lds, 32 * kk, db), tr.read(kt_lds, 32 * kk + 16, db));
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[qb][nb] = mfma_bf16(a[qb], b[nb], acc[qb][nb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = i0 + 32 * t + 16 * qb + 4 * g + i;
+        if (!RAGGED || q < nq) {
+          float* row = dQacc + hoffq + (size_t)q * D + wave * DW + l16;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            __hip_atomic_fetch_add(row + 16 * nb, acc[qb][nb][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+  };
 
   // One 32-query step t of a query tile has three stages:
   //   G1(t): S = Q K^T and dP = dO V^T          (2 D/32 MFMA groups of 2 NKB)
@@ -290,6 +375,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       }
       if constexpr (need_mask) ew_mask(i0, t, e);
       ew_end(e, pbuf[t & 1], sbuf[t & 1]);
+      if constexpr (FUSED) dq_step(sbuf[t & 1], i0, t, ds_lds + (t & 1) * BC * 32);
     }
     // epilogue: G2 of the last step alone
     {
@@ -311,13 +397,16 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                        __bf16* qn, __bf16* on, float* ln, float* dn, int it) __attribute__((always_inline)) {
     const int i0 = it * BR;
     if (it + 1 < it1) issue_tile(qn, on, ln, dn, i0 + BR);
-    const bool active = !CAUSAL || (i0 + BR - 1 + off >= k0w && (!BAND || i0 + lo < k0w + KW - 1));
+    // (fused: every wave takes part in the dQ product of every step, so the
+    // tests are made for the whole workgroup's keys)
+    const int kl = FUSED ? k0 : k0w, kw = FUSED ? BC : KW;
+    const bool active = !CAUSAL || (i0 + BR - 1 + off >= kl && (!BAND || i0 + lo < kl + kw - 1));
     if (active) {
       // only tiles crossing the diagonal, the window's edge or the end of the
       // sequence are masked; they run a separate copy so that the others carry
       // no mask arithmetic
       if ((CAUSAL || RAGGED) &&
-          ((CAUSAL && i0 + off < k0w + KW - 1) || (BAND && i0 + BR - 1 + lo >= k0w) || (i0 + BR > nq))) {
+          ((CAUSAL && i0 + off < kl + kw - 1) || (BAND && i0 + BR - 1 + lo >= kl) || (i0 + BR > nq))) {
         run_tile(qt, ot, lt, dt, i0, std::true_type{});
       } else {
         run_tile(qt, ot, lt, dt, i0, std::false_type{});
@@ -544,11 +633,11 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 }
 
-template <int D, int KW, int NW, int BR>
+template <int D, int KW, int NW, int BR, bool FUSED = false>
 static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, const void* dO,
                                    const float* lse, const float* delta, void* dk, void* dv,
                                    int bh, int nq, int nk, float scale, int causal, int window,
-                                   hipStream_t st) {
+                                   hipStream_t st, float* dqacc = nullptr) {
   constexpr int BC = KW * NW;
   const int ntk = (nk + BC - 1) / BC;
   const dim3 grid((unsigned)(ntk * bh)), block(NW * 64);
@@ -556,12 +645,50 @@ static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, 
   // the non-causal kernel keeps its masked copy even when nq is a multiple of
   // BR: the uniform branch around it splits the tile into scheduling regions
   // small enough to stay within the register file
-  auto kern = (causal && window > 0) ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, true>
-             : causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, false>
-                      : dkdv_bf16_kernel<D, KW, NW, BR, false, true, false>;
+  auto kern = (causal && window > 0) ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, true, FUSED>
+             : causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, false, FUSED>
+                      : dkdv_bf16_kernel<D, KW, NW, BR, false, true, false, FUSED>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, bh, nq, nk, window, scale,
-                     sl2);
+                     (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, dqacc, bh, nq, nk, window,
+                     scale, sl2);
+  return hipGetLastError();
+}
+
+// dQ = bf16(scale * acc), four values per thread (n is a multiple of 4)
+__global__ __launch_bounds__(256) void dq_from_acc_kernel(const float* __restrict__ acc,
+                                                          __bf16* __restrict__ dq, size_t n4,
+                                                          float scale) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(acc)[i];
+    bf16x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (__bf16)(a[j] * scale);
+    reinterpret_cast<bf16x4*>(dq)[i] = r;
+  }
+}
+
+// Single-kernel backward: zero the fp32 dQ accumulator, run the dK/dV kernel
+// with the fused dQ product, then round scale * acc to bf16.
+hipError_t launch_bwd_fused_bf16(const void* q, const void* k, const void* v, const void* dO,
+                                 const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                                 float* dq_acc, int bh, int nq, int nk, int d, float scale, int causal,
+                                 int window, int bm, int bn, hipStream_t st) {
+  const size_t n = (size_t)bh * nq * d;
+  hipError_t e = launch_zero_f32(dq_acc, n, st);
+  if (e != hipSuccess) return e;
+  if (d == 128 && bm == 64 && bn == 128)
+    e = launch_dkdv_inst<128, 32, 4, 64, true>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal,
+                                               window, st, dq_acc);
+  else if (d == 64 && bm == 64 && bn == 128)
+    e = launch_dkdv_inst<64, 32, 4, 64, true>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal,
+                                              window, st, dq_acc);
+  else
+    return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  const size_t blocks = std::min<size_t>((n / 4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(dq_from_acc_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dq_acc, (__bf16*)dq,
+                     n / 4, scale);
   return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@
 //
 // Tiles sit in LDS as [rows][D + 1] floats (odd row stride: the 16 rows a
 // fragment reads fall in distinct banks).
+#include <algorithm>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -133,12 +135,15 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL>
+// FUSED: also add scale * dS K into dQ (zeroed by the caller) with atomic
+// adds, the single-kernel backward: each wave moves its 16 x 16 dS block
+// through a private LDS tile so that dS is the A operand of dQ = dS K.
+template <int D, bool CAUSAL, bool FUSED = false>
 __global__ __launch_bounds__(512)
 void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                      const float* __restrict__ V, const float* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                     float* __restrict__ dK, float* __restrict__ dV,
+                     float* __restrict__ dK, float* __restrict__ dV, float* __restrict__ dQ,
                      int bh, int nq, int nk, int window, float scale, float scale_log2, int BR, int BC) {
   extern __shared__ float smem[];
   constexpr int LD = D + 1, NST = D / 4, NDB = D / 16;
@@ -216,6 +221,38 @@ void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
           for (int db = 0; db < NDB; ++db) {
             dv[db] = mfma_f32(or2[16 * db + l16], s[t], dv[db]);
             dk[db] = mfma_f32(qr2[16 * db + l16], dp[t], dk[db]);
+          }
+        }
+        if constexpr (FUSED) {
+          // dS block [query 4g + i][key l16] into the wave's tile, read back
+          // as A = dS[query l16][key 4st + g]; B = K[key 4st + g][16db + l16]
+          float* dsw = dsm + BR + wave * 16 * 17;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dsw[(4 * g + i) * 17 + l16] = dp[i];
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          float a[4];
+#pragma unroll
+          for (int st = 0; st < 4; ++st) a[st] = dsw[l16 * 17 + 4 * st + g];
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();   // reads done before the next block's writes
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              const int kr = k0w + 4 * st + g;
+              const float b = (kr < nk && kr < k0 + BC) ? K[hoffk + (size_t)kr * D + 16 * db + l16] : 0.f;
+              acc = mfma_f32(a[st], b, acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int qr = i0 + 16 * qb + 4 * g + i;
+              if (qr < nq)
+                __hip_atomic_fetch_add(dQ + hoffq + (size_t)qr * D + 16 * db + l16, acc[i] * scale,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
       }
@@ -316,6 +353,8 @@ size_t f32_lds_bytes(int kernel, int d, int bm, int bn) {
   const size_t ld = (size_t)d + 1;
   const size_t bcp = (size_t)((bn + 15) & ~15);
   if (kernel == 1) return (2 * (size_t)bm * ld + 2 * (size_t)bm) * sizeof(float);
+  if (kernel == 3)   // dK/dV with the fused dQ: one 16 x 17 dS tile per wave
+    return (2 * (size_t)bm * ld + 2 * (size_t)bm + (size_t)((bn + 15) / 16) * 16 * 17) * sizeof(float);
   return 2 * bcp * ld * sizeof(float);
 }
 
@@ -365,12 +404,48 @@ hipError_t launch_dkdv_f32(const float* q, const float* k, const float* v, const
     auto kern = causal ? dkdv_f32_kernel<DD, true> : dkdv_f32_kernel<DD, false>;            \
     hipError_t e = set_lds(kern, lds);                                                      \
     if (e != hipSuccess) return e;                                                          \
-    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dk, dv, bh, nq, \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dk, dv,         \
+                       (float*)nullptr, bh, nq,                                             \
                        nk, window,                                                          \
                        scale, sl2, bm, bn);                                                 \
   }
   FA_F32_DISPATCH_D(FA_DKDV_F32)
 #undef FA_DKDV_F32
+  return hipGetLastError();
+}
+
+// p[0 .. n) = 0 with a kernel (not hipMemsetAsync), so that a captured graph
+// replays it like any other node.
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st) {
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused_f32(const float* q, const float* k, const float* v, const float* dO,
+                                const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                                int bh, int nq, int nk, int d, float scale, int causal, int window,
+                                int bm, int bn, hipStream_t st) {
+  hipError_t e = launch_zero_f32(dq, (size_t)bh * nq * d, st);
+  if (e != hipSuccess) return e;
+  const size_t lds = f32_lds_bytes(3, d, bm, bn);
+  const dim3 grid((unsigned)(((nk + bn - 1) / bn) * bh)), block(((bn + 15) / 16) * 64);
+  const float sl2 = scale * kLog2e;
+#define FA_FUSED_F32(DD)                                                                    \
+  {                                                                                         \
+    auto kern = causal ? dkdv_f32_kernel<DD, true, true> : dkdv_f32_kernel<DD, false, true>; \
+    e = set_lds(kern, lds);                                                                 \
+    if (e != hipSuccess) return e;                                                          \
+    hipLaunchKernelGGL(kern, grid, block, lds, st, q, k, v, dO, lse, delta, dk, dv, dq, bh, \
+                       nq, nk, window, scale, sl2, bm, bn);                                 \
+  }
+  FA_F32_DISPATCH_D(FA_FUSED_F32)
+#undef FA_FUSED_F32
   return hipGetLastError();
 }
 

@@ -37,6 +37,22 @@ hipError_t launch_dq_f32(const float* q, const float* k, const float* v, const f
                          int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                          hipStream_t st);
 
+// Single-kernel backward (dK, dV and dQ in one pass over the key tiles, dQ
+// accumulated with fp32 atomic adds).  bf16: dq_acc is an fp32 workspace of
+// bh * nq * d floats that the call clears and then rounds into dq; float32:
+// dq itself is cleared and accumulated.  Tilings: the dK/dV ones whose query
+// tile is 64 rows (bf16), any dK/dV tiling (float32).
+hipError_t launch_bwd_fused_bf16(const void* q, const void* k, const void* v, const void* dO,
+                                 const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                                 float* dq_acc, int bh, int nq, int nk, int d, float scale, int causal,
+                                 int window, int bm, int bn, hipStream_t st);
+hipError_t launch_bwd_fused_f32(const float* q, const float* k, const float* v, const float* dO,
+                                const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                                int bh, int nq, int nk, int d, float scale, int causal, int window,
+                                int bm, int bn, hipStream_t st);
+// p[0 .. n) = 0 (a fill kernel, safe under graph capture)
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
+
 // dtype: 0 = float32, 1 = bf16
 hipError_t launch_preprocess(const void* o, const void* dO, float* delta, int bh, int nq, int d,
                              int dtype, hipStream_t st);

@@ -18,6 +18,9 @@
  *                      a chunk of new queries against a longer key/value
  *                      cache, and an optional causal sliding window;
  *                      fa_bwd_preprocess serves both forms.
+ *   fa_bwd_fused       the single-kernel backward that the two-kernel form
+ *                      is weighed against: dK, dV and dQ from one pass over
+ *                      the key/value tiles, dQ gathered with atomic adds.
  *
  * Source of the method (cited by page and section):
  *   "Assignment2: FlashAttention & Distributed Data Parallel notes"
@@ -81,11 +84,13 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
@@ -144,8 +149,33 @@ fa_status fa_bwd_dq_rect(const void* q, const void* k, const void* v, const void
                          int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
                          int causal, int window, int block_m, int block_n, void* stream);
 
+/* Single-kernel backward (the alternative to steps 2 and 3 that CS336 notes
+ * 1.4 sets aside: one kernel with dQ accumulated by atomic adds).  One pass
+ * over the key/value tiles writes dk and dv exactly as fa_bwd_dkdv_rect
+ * does and adds each (key tile, query tile) pair's dS K into dQ with float32
+ * atomic adds, so dQ depends on the order in which the adds land (not
+ * bitwise reproducible) and P is rebuilt once instead of twice.  Arguments
+ * as fa_bwd_dkdv_rect plus dq ([bh][nq][d], `dtype`) and `workspace`:
+ * FA_BF16 accumulates dQ in float32 in `workspace`
+ * (fa_bwd_fused_workspace_bytes bytes of device memory, 16-byte aligned,
+ * distinct from every other buffer; its contents on entry are ignored and
+ * on return unspecified) and rounds scale * dQ to bf16 into dq at the end;
+ * FA_F32 accumulates in dq itself and ignores `workspace` (may be NULL).
+ * Tilings: kernel id 3 of fa_default_tiles (bf16: block_m = 64 query rows
+ * per step, block_n = 128 keys per workgroup; float32: as fa_bwd_dkdv within
+ * the LDS budget).  Needs delta from fa_bwd_preprocess like steps 2 and 3. */
+fa_status fa_bwd_fused(const void* q, const void* k, const void* v, const void* dO,
+                       const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                       float* workspace, int bh, int nq, int nk, int d, fa_dtype dtype,
+                       float scale, int causal, int window, int block_m, int block_n,
+                       void* stream);
+/* Bytes of `workspace` fa_bwd_fused needs: bh * nq * d * 4 for FA_BF16, 0 for
+ * FA_F32 (and 0 for non-positive sizes).  Pure host function. */
+size_t fa_bwd_fused_workspace_bytes(int bh, int nq, int d, fa_dtype dtype);
+
 /* The tiling (block_m, block_n) that block_m = block_n = 0 selects for a
- * kernel (0 = fwd, 1 = dkdv, 2 = dq) at this dtype and head dim.  Returns
+ * kernel (0 = fwd, 1 = dkdv, 2 = dq, 3 = fused backward) at this dtype and
+ * head dim.  Returns
  * FA_ERR_UNSUPPORTED for a head dim or dtype the library does not provide.  Pure
  * host function. */
 fa_status fa_default_tiles(fa_dtype dtype, int d, int kernel, int* block_m, int* block_n);

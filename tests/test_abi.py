@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     for code in range(5):
         assert fa.fa_status_str(code)
     assert fa.fa_status_str(99) == "unknown status"
@@ -225,3 +225,50 @@ def test_autograd_op_validates_on_host():
         fa.flash_attention(q, q[:1], q[:1])              # leading dims must agree
     with pytest.raises(ValueError):
         fa.flash_attention(q[0, 0], q[0, 0], q[0, 0])    # needs [..., n, d]
+
+
+# --------------------------------------------------------------------------- fused backward
+W = 0x90000   # fake workspace address
+
+
+def fused(lib, **kw):
+    a = dict(q=A, k=B, v=C, dO=D_, lse=E, delta=F, dq=G, dk=H, dv=0xA0000, ws=W, bh=1, nq=64, nk=128, d=64,
+             dtype=fa.FA_BF16, scale=0.125, causal=1, window=0, bm=0, bn=0)
+    a.update(kw)
+    return lib.fa_bwd_fused(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dq"], a["dk"], a["dv"],
+                            a["ws"], a["bh"], a["nq"], a["nk"], a["d"], a["dtype"], a["scale"], a["causal"],
+                            a["window"], a["bm"], a["bn"], None)
+
+
+def test_fused_workspace_bytes(lib):
+    assert fa.fa_bwd_fused_workspace_bytes(32, 8192, 128, fa.FA_BF16) == 32 * 8192 * 128 * 4
+    assert fa.fa_bwd_fused_workspace_bytes(32, 8192, 128, fa.FA_F32) == 0
+    assert fa.fa_bwd_fused_workspace_bytes(0, 8192, 128, fa.FA_BF16) == 0
+    assert fa.fa_bwd_fused_workspace_bytes(-1, 8192, 128, fa.FA_BF16) == 0
+    # no 32-bit overflow at the largest sizes
+    assert fa.fa_bwd_fused_workspace_bytes(1 << 20, 1 << 24, 128, fa.FA_BF16) == (1 << 20) * (1 << 24) * 512
+
+
+def test_fused_tiles(lib):
+    assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_FUSED) == (64, 128)
+    assert fa.fa_default_tiles(fa.FA_BF16, 64, fa.KERNEL_FUSED) == (64, 128)
+    assert fa.fa_default_tiles(fa.FA_F32, 32, fa.KERNEL_FUSED) == (64, 64)
+    # the 128-query bf16 dK/dV tiling does not leave LDS for the fused dQ operands
+    assert fused(lib, d=128, bm=128, bn=128) == fa.FA_ERR_UNSUPPORTED
+    assert fused(lib, dtype=fa.FA_F32, d=128, bm=48, bn=64) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fused_argument_checks(lib):
+    assert fused(lib, ws=0) == fa.FA_ERR_INVALID_ARG                 # bf16 needs the workspace
+    assert fused(lib, ws=W + 4) == fa.FA_ERR_MISALIGNED
+    assert fused(lib, ws=G) == fa.FA_ERR_INVALID_ARG                 # workspace is dq
+    assert fused(lib, ws=A) == fa.FA_ERR_INVALID_ARG                 # workspace is q
+    assert fused(lib, dq=A) == fa.FA_ERR_INVALID_ARG
+    assert fused(lib, dq=H) == fa.FA_ERR_INVALID_ARG                 # dq is dk
+    assert fused(lib, dq=0) == fa.FA_ERR_INVALID_ARG
+    assert fused(lib, window=-1) == fa.FA_ERR_INVALID_ARG
+    assert fused(lib, window=5, causal=0) == fa.FA_ERR_INVALID_ARG
+    assert fused(lib, nq=129, nk=128) == fa.FA_ERR_UNSUPPORTED
+    assert fused(lib, scale=0.0) == fa.FA_ERR_INVALID_ARG
+    assert fused(lib, bh=0, q=0, ws=0) == fa.FA_OK
+    assert fused(lib, d=96) == fa.FA_ERR_UNSUPPORTED

@@ -383,3 +383,102 @@ def test_window_rejects_bad_arguments():
         run_gpu(arrays, "bf16", False, window=16)
     with pytest.raises(fa.FAError):
         run_gpu(arrays, "bf16", True, window=-1)
+
+
+# --------------------------------------------------------------------------- single-kernel backward
+# fa_bwd_fused: dK, dV and dQ from one pass over the key tiles, dQ gathered
+# with fp32 atomic adds (the design the two-kernel backward is weighed
+# against).  Same oracle and tolerances as the two-kernel path.
+def run_gpu_fused(arrays, dtype, causal, tiles=(0, 0), window=0, fwd_tiles=(0, 0)):
+    q, k, v, do = cast_io(arrays, dtype, "cuda")
+    o, lse = fa.forward(q, k, v, causal, None, *fwd_tiles, window=window)
+    dq, dk, dv, delta = fa.backward_fused(q, k, v, o, do, lse, causal, None, tiles, window=window)
+    torch.cuda.synchronize()
+    return {name: to_f64(t) for name, t in
+            dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta).items()}
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tiles", [(16, 12), (64, 64), (32, 128)])
+def test_fused_fp32(causal, tiles):
+    arrays = make_inputs(2, 200, 32, seed=50)
+    g = run_gpu_fused(arrays, "fp32", causal, tiles)
+    compare_full(g, "fp32", causal, label=f"fused fp32 n=200 tiles={tiles} causal={causal}")
+
+
+@pytest.mark.parametrize("nq,nk,causal,window", [(37, 100, True, 0), (200, 64, False, 0), (64, 200, True, 33),
+                                                 (200, 200, True, 17)])
+def test_fused_fp32_rect_and_window(nq, nk, causal, window):
+    arrays = make_rect_inputs(2, nq, nk, 32, seed=51)
+    g = run_gpu_fused(arrays, "fp32", causal, (16, 12), window=window)
+    compare_full(g, "fp32", causal, label=f"fused fp32 {nq}x{nk} causal={causal} window={window}", window=window)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [100, 333, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fused_bf16(d, n, causal):
+    arrays = make_inputs(2, n, d, seed=52)
+    g = run_gpu_fused(arrays, "bf16", causal)
+    compare_full(g, "bf16", causal, label=f"fused bf16 d={d} n={n} causal={causal}")
+    # dK and dV come from the same arithmetic as fa_bwd_dkdv
+    ref = run_gpu(arrays, "bf16", causal)
+    for name in ("dk", "dv"):
+        assert np.abs(g[name] - ref[name]).max() <= 1e-2 * max(1.0, np.abs(ref[name]).max()), name
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nq,nk,causal,window", [(300, 1000, True, 0), (500, 200, False, 0),
+                                                 (256, 4096, True, 1000), (1000, 1000, True, 100)])
+def test_fused_bf16_rect_and_window(d, nq, nk, causal, window):
+    arrays = make_rect_inputs(2, nq, nk, d, seed=53)
+    g = run_gpu_fused(arrays, "bf16", causal, window=window)
+    compare_full(g, "bf16", causal, label=f"fused bf16 d={d} {nq}x{nk} causal={causal} window={window}",
+                 window=window)
+
+
+def test_fused_sampled_8192():
+    """BH = 32, N = 8192, d = 128, bf16, causal through the fused backward at
+    the default tiling; sampled rows and columns against the oracle."""
+    w = WORKLOADS["headline_8192_d128"]
+    arrays = make_inputs(w.bh, w.n, w.d, seed=0)
+    g = run_gpu_fused(arrays, w.dtype, True)
+    rng = np.random.default_rng(96)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 4095, 8191], rng.integers(0, w.n, 16)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 8191], rng.integers(0, w.n, 8)]))
+    tol = TOL[w.dtype]
+    for h in (0, 17):
+        q, k, v, do = (g[x][h] for x in ("q", "k", "v", "do"))
+        dq_ref, _ = oracle.dq_rows(q, k, v, do, rows, causal=True)
+        stats = oracle.head_row_stats(q, k, v, do, causal=True)
+        dk_ref, dv_ref = oracle.dkdv_cols(q, k, v, do, cols, causal=True, stats=stats)
+        rep = {
+            "dq": np.abs(g["dq"][h][rows] - dq_ref).max() / np.abs(g["dq"][h]).max(),
+            "dk": np.abs(g["dk"][h][cols] - dk_ref).max() / np.abs(g["dk"][h]).max(),
+            "dv": np.abs(g["dv"][h][cols] - dv_ref).max() / np.abs(g["dv"][h]).max(),
+        }
+        _say(f"[fused 8192 head={h}] " + " ".join(f"{a}={b:.2e}" for a, b in rep.items()))
+        for name in rep:
+            assert rep[name] <= tol["grad"], (name, rep)
+    for name in ("dq", "dk", "dv"):
+        assert np.all(np.isfinite(g[name])), name
+
+
+def test_fused_workspace_contents_do_not_matter():
+    """The call clears its workspace itself: garbage in it changes nothing
+    beyond the order of the atomic adds."""
+    arrays = make_inputs(2, 300, 128, seed=54)
+    q, k, v, do = cast_io(arrays, "bf16", "cuda")
+    o, lse = fa.forward(q, k, v, True)
+    delta = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    fa.fa_bwd_preprocess(o, do, delta)
+    outs = []
+    for fill in (0.0, 1e30):
+        ws = torch.full((fa.fa_bwd_fused_workspace_bytes(2, 300, 128, fa.FA_BF16) // 4,), fill,
+                        dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        fa.fa_bwd_fused(q, k, v, do, lse, delta, dq, dk, dv, ws, True)
+        torch.cuda.synchronize()
+        outs.append(to_f64(dq))
+    scale = np.abs(outs[0]).max()
+    assert np.abs(outs[0] - outs[1]).max() <= 1e-2 * scale
