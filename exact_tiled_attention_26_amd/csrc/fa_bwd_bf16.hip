@@ -21,8 +21,12 @@
 //   in registers.  Key tiles of K and V are staged through LDS.  S^T and dP^T
 //   (keys x queries) feed dQ^T += K^T dS^T with K^T read transposed from LDS.
 // * Causal mode visits only the tiles that hold a visible (query, key) pair
-//   and masks only tiles crossing the diagonal.  Workgroups are ordered with
-//   the heaviest tiles first.
+//   and masks only tiles crossing the diagonal; a sliding window (BAND
+//   instances) also bounds the loops from the band's other edge.  Workgroups
+//   are ordered with the heaviest tiles first.
+// * The FUSED instance of the dK/dV kernel is the single-kernel alternative
+//   (one pass, dQ gathered with fp32 atomic adds) that section 1.4 sets
+//   aside; it is kept for comparison and measured slower on this device.
 #include <algorithm>
 #include <type_traits>
 

@@ -7,7 +7,9 @@
 // 1.3 -- one workgroup per (head, query tile); key tiles that start after the
 // tile's last query are skipped in causal mode.  Only tiles crossing the
 // diagonal are masked ("CS349E lecture 11, 03_flash_backward.py",
-// demo4_causal).
+// demo4_causal).  With a sliding window ("CS324 lecture 8,
+// 03_online_softmax_and_flash.py", window_attention_torch) tiles wholly
+// before the band are skipped too and its lower edge is masked the same way.
 //
 // Mapping onto gfx950:
 // * A workgroup owns BR = NW * QW query rows of one head; wave w owns QW rows.
