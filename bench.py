@@ -73,12 +73,23 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without comments and blank lines (string literals in these
+    kernels hold no comment markers)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def source_hash(kernel):
+    """SHA-1 (12 hex digits) of the kernel's source files with comments
+    removed, so that editing a comment keeps the recorded counters valid."""
     import hashlib
     h = hashlib.sha1()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "exact_tiled_attention_26_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "exact_tiled_attention_26_amd", "csrc", f)) as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:12]
 
 
