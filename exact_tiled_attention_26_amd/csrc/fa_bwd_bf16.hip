@@ -446,8 +446,11 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   }
 }
 
+// Occupancy: with 32-key tiles the kernel fits two waves per SIMD (at most
+// 256 registers each), so the matrix products of one wave overlap the
+// element-wise work of the other; with 64-key tiles it holds one.
 template <int D, int QW, int NW, int BC, bool CAUSAL, bool BAND>
-__global__ __launch_bounds__(NW * 64, 1)
+__global__ __launch_bounds__(NW * 64, BC == 32 ? 2 : 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                     const float* __restrict__ LSE, const float* __restrict__ DELTA,
@@ -732,6 +735,8 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
                           const float* lse, const float* delta, void* dq,
                           int bh, int nq, int nk, int d, float scale, int causal, int window, int bm, int bn,
                           hipStream_t st) {
+  if (d == 128 && bm == 128 && bn == 32)
+    return launch_dq_inst<128, 32, 4, 32>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   if (d == 128 && bm == 128 && bn == 64)
     return launch_dq_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   if (d == 64 && bm == 128 && bn == 64)

@@ -128,12 +128,17 @@ def test_bf16_2048_d64_noncausal():
     compare_full(g, "bf16", False, label="bf16 8x2048x64 non-causal")
 
 
+# every bf16 d = 128 tiling: forward (128, 64) and (256, 64), dK/dV (64, 128)
+# and (128, 128), dQ (128, 32) and (128, 64)
+BF16_D128_TILINGS = [((128, 64), (64, 128), (128, 32)), ((256, 64), (128, 128), (128, 64))]
+
+
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("fwd_tiles", [(128, 64), (256, 64)])
-def test_bf16_d128_small(causal, fwd_tiles):
+@pytest.mark.parametrize("tiles", BF16_D128_TILINGS)
+def test_bf16_d128_small(causal, tiles):
     arrays = make_inputs(4, 1024, 128, seed=2)
-    g = run_gpu(arrays, "bf16", causal, fwd_tiles)
-    compare_full(g, "bf16", causal, label=f"bf16 4x1024x128 fwd{fwd_tiles} causal={causal}")
+    g = run_gpu(arrays, "bf16", causal, *tiles)
+    compare_full(g, "bf16", causal, label=f"bf16 4x1024x128 tiles={tiles} causal={causal}")
 
 
 # --------------------------------------------------------------------------- ragged / edge
@@ -329,13 +334,12 @@ def test_window_bf16(d, window, n):
     compare_full(g, "bf16", True, label=f"bf16 d={d} n={n} window={window}", window=window)
 
 
-@pytest.mark.parametrize("fwd_tiles,dkdv_tiles", [((128, 64), (128, 128)), ((256, 64), (64, 128))])
+@pytest.mark.parametrize("tiles", BF16_D128_TILINGS)
 @pytest.mark.parametrize("window", [50, 300])
-def test_window_bf16_tilings(fwd_tiles, dkdv_tiles, window):
+def test_window_bf16_tilings(tiles, window):
     arrays = make_inputs(2, 1000, 128, seed=43)
-    g = run_gpu(arrays, "bf16", True, fwd_tiles, dkdv_tiles, window=window)
-    compare_full(g, "bf16", True, label=f"bf16 window={window} tiles={fwd_tiles},{dkdv_tiles}",
-                 window=window)
+    g = run_gpu(arrays, "bf16", True, *tiles, window=window)
+    compare_full(g, "bf16", True, label=f"bf16 window={window} tiles={tiles}", window=window)
 
 
 @pytest.mark.parametrize("nq,nk,window", [(300, 1000, 128), (256, 4096, 1000), (1, 513, 100)])
