@@ -3,6 +3,9 @@
 Usage: ``python -m exact_tiled_attention_26_amd.build`` or ``build()`` from
 Python.  Every source under ``csrc/`` is compiled with hipcc for gfx950 into
 ``_build/`` (in parallel) and linked into ``libfa.so`` next to this file.
+``build_c_client()`` also compiles the plain C client of the ABI that the
+tests run (``tests/c_abi/fa_c_client.c``, host code only, linked against
+libfa.so).
 """
 
 from __future__ import annotations
@@ -65,6 +68,32 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return LIB
 
 
+ROOT = os.path.dirname(HERE)
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi", "fa_c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_abi", "_build", "fa_c_client")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile the C99 client of include/fa.h with the host C compiler; it
+    finds libfa.so next to this file through a relative run path."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler (gcc) for the C client of the ABI")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    os.makedirs(os.path.dirname(C_CLIENT), exist_ok=True)
+    rpath = "$ORIGIN/" + os.path.relpath(HERE, os.path.dirname(C_CLIENT))
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+           f"-I{os.path.join(ROOT, 'include')}", C_CLIENT_SRC, f"-L{HERE}", "-lfa", f"-L{rocm}/lib",
+           "-lamdhip64", f"-Wl,-rpath,{rpath}:{rocm}/lib", "-lm", "-o", C_CLIENT]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C client build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_CLIENT}")
+    return C_CLIENT
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_client(verbose=True)
     sys.exit(0)

@@ -272,3 +272,18 @@ def test_fused_argument_checks(lib):
     assert fused(lib, scale=0.0) == fa.FA_ERR_INVALID_ARG
     assert fused(lib, bh=0, q=0, ws=0) == fa.FA_OK
     assert fused(lib, d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------- plain C client
+def test_c_client_links_and_reports_abi(lib):
+    """The C99 client of include/fa.h (built by build()) links against
+    libfa.so and calls its host-only functions without Python in between."""
+    import subprocess
+    from exact_tiled_attention_26_amd.build import C_CLIENT
+    assert os.path.exists(C_CLIENT), "build the C client first (__graft_entry__.build())"
+    r = subprocess.run([C_CLIENT, "--abi"], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[:2] == ["abi", str(fa.fa_abi_version())]
+    # bad arguments are refused before any HIP call
+    r = subprocess.run([C_CLIENT, "in", "out", "0", "8", "64", "1"], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1
