@@ -181,6 +181,11 @@ __device__ __forceinline__ void lds_dma16(const void* gbase, unsigned byte_off, 
   __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                    :: "v"(byte_off), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_address(lds))) : "memory");
 }
+// The same with the LDS destination given as a byte address.
+__device__ __forceinline__ void lds_dma16_at(const void* gbase, unsigned byte_off, unsigned lds_byte) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(byte_off), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_byte)) : "memory");
+}
 
 // Asynchronous copy of a ROWS x D bf16 tile (global, row stride D) into a
 // swizzled LDS tile with global_load_lds_dwordx4: lane i of a wave writes the
@@ -222,6 +227,29 @@ struct AsyncTileCopy {
         const int off = row < valid ? src_off[i] : src_off[i] - (row - valid + 1) * D;
         issue_one(tile + lds_off[i], g, off);
       }
+    }
+  }
+  // Same as issue() with the tile given by its LDS byte address (uniform),
+  // which spares the kernel a generic pointer per buffer.
+  __device__ __forceinline__ void issue_at(unsigned tile_byte, const __bf16* g, int valid) const {
+    if (valid >= ROWS) {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) issue_one_at(tile_byte + 2u * lds_off[i], g, src_off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int row = src_off[i] / D;
+        const int off = row < valid ? src_off[i] : src_off[i] - (row - valid + 1) * D;
+        issue_one_at(tile_byte + 2u * lds_off[i], g, off);
+      }
+    }
+  }
+  __device__ __forceinline__ static void issue_one_at(unsigned lds_byte, const __bf16* g, int off) {
+    if constexpr (HIDDEN) {
+      lds_dma16_at(g, 2u * off, lds_byte);
+    } else {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
+                                       (__attribute__((address_space(3))) void*)(uintptr_t)lds_byte, 16, 0, 0);
     }
   }
   __device__ __forceinline__ static void issue_one(__bf16* lds, const __bf16* g, int off) {

@@ -97,9 +97,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int last = CAUSAL ? min(ntk - 1, (q0w + QW - 1 + off) / BC) : ntk - 1 + dz;
   const AsyncTileCopy<D, BC, NW> copier(wave, lane);
   // buffers are indexed by the tile's position t - jt0 in the loop
-  copier.issue(k_lds[0], Kh + (size_t)jt0 * BC * D, nk - jt0 * BC);
-  if (jt0 + 1 < ntk) copier.issue(k_lds[1], Kh + (size_t)(jt0 + 1) * BC * D, nk - (jt0 + 1) * BC);
-  copier.issue(v_lds[0], Vh + (size_t)jt0 * BC * D, nk - jt0 * BC);
+  // LDS byte addresses of the buffers: the copies take these, not pointers
+  constexpr unsigned TB = BC * D * 2;
+  const unsigned kbase = lds_address(&k_lds[0][0]), vbase = lds_address(&v_lds[0][0]);
+  copier.issue_at(kbase, Kh + (size_t)jt0 * BC * D, nk - jt0 * BC);
+  if (jt0 + 1 < ntk) copier.issue_at(kbase + TB, Kh + (size_t)(jt0 + 1) * BC * D, nk - (jt0 + 1) * BC);
+  copier.issue_at(vbase, Vh + (size_t)jt0 * BC * D, nk - jt0 * BC);
 
   // Q rows of this wave as B operands: lane holds Q[q0w + 16qb + l16][32ds + 8g .. +7]
   bf16x8 qf[NQB][NDS];
@@ -215,8 +218,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   async_copy_wait();
   // copies that step 0 waits for when the distance is two steps
   if constexpr (NBUF == 3) {
-    if (jt0 + 1 < ntk) copier.issue(v_lds[1], Vh + (size_t)(jt0 + 1) * BC * D, nk - (jt0 + 1) * BC);
-    if (jt0 + 2 < ntk) copier.issue(k_lds[2], Kh + (size_t)(jt0 + 2) * BC * D, nk - (jt0 + 2) * BC);
+    if (jt0 + 1 < ntk) copier.issue_at(vbase + TB, Vh + (size_t)(jt0 + 1) * BC * D, nk - (jt0 + 1) * BC);
+    if (jt0 + 2 < ntk) copier.issue_at(kbase + 2 * TB, Kh + (size_t)(jt0 + 2) * BC * D, nk - (jt0 + 2) * BC);
   }
   __syncthreads();
   // (a wave whose band starts later computes its first scores in the step before)
@@ -332,8 +335,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int r = t - jt0;
     const int b0 = r % NBUF, b1 = (r + 1) % NBUF, bl = (r + NBUF - 1) % NBUF;
     const bool ck = t + NBUF < ntk, cv = t + NBUF - 1 < ntk;
-    if (cv) copier.issue(v_lds[bl], Vh + (size_t)(t + NBUF - 1) * BC * D, nk - (t + NBUF - 1) * BC);
-    if (ck) copier.issue(k_lds[b0], Kh + (size_t)(t + NBUF) * BC * D, nk - (t + NBUF) * BC);
+    if (cv) copier.issue_at(vbase + bl * TB, Vh + (size_t)(t + NBUF - 1) * BC * D, nk - (t + NBUF - 1) * BC);
+    if (ck) copier.issue_at(kbase + b0 * TB, Kh + (size_t)(t + NBUF) * BC * D, nk - (t + NBUF) * BC);
     if (t <= last && (!BAND || t >= first)) {
       const __bf16* kn = k_lds[b1];
       const __bf16* vt = v_lds[b0];
