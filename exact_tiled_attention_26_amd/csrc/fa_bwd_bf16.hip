@@ -100,6 +100,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const float* Dh = DELTA + (size_t)head * nq;
 
   const int ntq = (nq + BR - 1) / BR;
+  const int dz = divergent_zero();   // keeps the compiler from merging the masked and unmasked tiles
   const int it0 = CAUSAL ? max(0, k0 - off) / BR : 0;   // earlier query rows see none of these keys
   // later rows see none of them either once the window has moved past them
   const int it1 = BAND ? min(ntq, max(0, k0 + BC - 2 - lo) / BR + 1) : ntq;
@@ -410,7 +411,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       // sequence are masked; they run a separate copy so that the others carry
       // no mask arithmetic
       if ((CAUSAL || RAGGED) &&
-          ((CAUSAL && i0 + off < kl + kw - 1) || (BAND && i0 + BR - 1 + lo >= kl) || (i0 + BR > nq))) {
+          ((CAUSAL && i0 + off < kl + kw - 1) || (BAND && i0 + BR - 1 + lo >= kl) || (i0 + BR > nq + dz))) {
         run_tile(qt, ot, lt, dt, i0, std::true_type{});
       } else {
         run_tile(qt, ot, lt, dt, i0, std::false_type{});
