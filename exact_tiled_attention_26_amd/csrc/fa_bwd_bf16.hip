@@ -234,7 +234,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   constexpr int NG1 = 2 * NDS;                   // MFMA groups of G1: (ds, h)
   constexpr int NG2 = NDB;                       // MFMA groups of G2: db
   constexpr int NE = 2 * 4 * NKB;                // elementwise items per lane per step
-  constexpr int PF = 2;                          // operand prefetch distance (groups)
+  constexpr int PF = 3;                          // operand prefetch distance (groups)
 
   struct EwState {
     float l2[2][4], dd[2][4];
