@@ -22,23 +22,23 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def _buffers(bh, n, d, seed):
-    q, k, v, do = cast_io(make_inputs(bh, n, d, seed=seed), "bf16", "cuda")
+def _buffers(bh, n, d, seed, dtype="bf16"):
+    q, k, v, do = cast_io(make_inputs(bh, n, d, seed=seed), dtype, "cuda")
     lse = torch.empty((bh, n), dtype=torch.float32, device="cuda")
     delta = torch.empty_like(lse)
     outs = dict(o=torch.empty_like(q), dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
     return q, k, v, do, lse, delta, outs
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_graph_replays_match_eager(fused):
-    _say(f"graph capture fused={fused}")
-    bh, n, d = 4, 1000, 128
-    q, k, v, do, lse, delta, b = _buffers(bh, n, d, seed=60)
+@pytest.mark.parametrize("dtype,fused", [("bf16", False), ("bf16", True), ("fp32", False), ("fp32", True)])
+def test_graph_replays_match_eager(dtype, fused):
+    _say(f"graph capture dtype={dtype} fused={fused}")
+    bh, n, d = (4, 1000, 128) if dtype == "bf16" else (2, 300, 64)
+    q, k, v, do, lse, delta, b = _buffers(bh, n, d, seed=60, dtype=dtype)
     ws = None
-    if fused:
-        ws = torch.empty(fa.fa_bwd_fused_workspace_bytes(bh, n, d, fa.FA_BF16) // 4, dtype=torch.float32,
-                         device="cuda")
+    nbytes = fa.fa_bwd_fused_workspace_bytes(bh, n, d, fa.FA_BF16 if dtype == "bf16" else fa.FA_F32)
+    if fused and nbytes:
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
 
     def step():
         fa.fa_fwd(q, k, v, b["o"], lse, True)
@@ -71,6 +71,7 @@ def test_graph_replays_match_eager(fused):
             got = to_f64(t)
             if fused and name == "dq":
                 scale = np.abs(eager[name]).max()
-                assert np.abs(got - eager[name]).max() <= 1e-2 * scale, (replay, name)
+                tol = 1e-2 if dtype == "bf16" else 1e-5
+                assert np.abs(got - eager[name]).max() <= tol * scale, (replay, name)
             else:
                 assert np.array_equal(got, eager[name]), (replay, name)
