@@ -58,6 +58,10 @@ WORKLOADS = {
     "long_32768_d128": Workload(
         "long_32768_d128", 8, 32768, 128, "bf16", (True,), (),
         "long context; only L is saved, never P"),
+    # throughput of the float32 kernels (not one of the pages' configurations)
+    "fp32_4096_d64": Workload(
+        "fp32_4096_d64", 16, 4096, 64, "fp32", (True, False), (),
+        "float32 I/O and products, for the float32 kernels' throughput"),
 }
 
 
