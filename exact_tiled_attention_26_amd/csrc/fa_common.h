@@ -177,12 +177,8 @@ struct TrReader {
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-__device__ __forceinline__ void lds_dma16(const void* gbase, unsigned byte_off, const void* lds) {
-  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                   :: "v"(byte_off), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_address(lds))) : "memory");
-}
-// The same with the LDS destination given as a byte address.
-__device__ __forceinline__ void lds_dma16_at(const void* gbase, unsigned byte_off, unsigned lds_byte) {
+// lds_byte: the wave's LDS destination (byte address, uniform).
+__device__ __forceinline__ void lds_dma16(const void* gbase, unsigned byte_off, unsigned lds_byte) {
   __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                    :: "v"(byte_off), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_byte)) : "memory");
 }
@@ -246,7 +242,7 @@ struct AsyncTileCopy {
   }
   __device__ __forceinline__ static void issue_one_at(unsigned lds_byte, const __bf16* g, int off) {
     if constexpr (HIDDEN) {
-      lds_dma16_at(g, 2u * off, lds_byte);
+      lds_dma16(g, 2u * off, lds_byte);
     } else {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
                                        (__attribute__((address_space(3))) void*)(uintptr_t)lds_byte, 16, 0, 0);
@@ -254,7 +250,7 @@ struct AsyncTileCopy {
   }
   __device__ __forceinline__ static void issue_one(__bf16* lds, const __bf16* g, int off) {
     if constexpr (HIDDEN) {
-      lds_dma16(g, 2u * off, lds);
+      lds_dma16(g, 2u * off, lds_address(lds));
     } else {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
                                        (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
