@@ -136,7 +136,9 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
  * j <= i + (nk - nq) - window, so each query sees its `window` most recent
  * keys; key tiles wholly outside the band are skipped and only tiles that
  * cross one of its edges are masked.  window == 0 means no window;
- * window < 0, or window > 0 without causal, is FA_ERR_INVALID_ARG. */
+ * window < 0, or window > 0 without causal, is FA_ERR_INVALID_ARG.  With a
+ * window (narrower than nk) and block_m = block_n = 0, the bf16 forward at
+ * d = 128 uses the (128, 64) tiling instead of fa_default_tiles' (256, 64). */
 fa_status fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
                       int bh, int nq, int nk, int d, fa_dtype dtype, float scale, int causal,
                       int window, int block_m, int block_n, void* stream);
