@@ -410,11 +410,10 @@ def _torch_rect_reference(q, k, v, do, causal, scale):
     return out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
 
 
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("nq,nk", [(37, 100), (1, 64), (64, 64), (90, 31)])
+# (causal with more queries than keys is rejected by the oracle: test below)
+@pytest.mark.parametrize("causal,nq,nk", [(c, nq, nk) for nq, nk in ((37, 100), (1, 64), (64, 64), (90, 31))
+                                          for c in (False, True) if not (c and nq > nk)])
 def test_rect_matches_torch_sdpa_mask(causal, nq, nk):
-    if causal and nq > nk:
-        pytest.skip("causal needs nq <= nk")
     rng = np.random.default_rng(21)
     d = 8
     q, do = (rng.standard_normal((nq, d)) for _ in range(2))
