@@ -6,13 +6,16 @@
  *   fa_c_client --abi
  *       prints FA_ABI_VERSION of the loaded library and a status string
  *       (host only, no GPU needed).
- *   fa_c_client IN OUT BH N D CAUSAL
+ *   fa_c_client IN OUT BH N D CAUSAL [WINDOW FUSED]
  *       reads q, k, v, dO (bf16, each BH * N * D values, raw, in that order)
  *       from IN, runs fa_fwd, fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq on
  *       the default stream with the default tilings and scale 1/sqrt(D), and
  *       writes o (bf16), lse (float32, BH * N), dq, dk, dv (bf16) and delta
- *       (float32) to OUT.  Also checks that an unsupported head dim is
- *       rejected before any launch.  Exit status 0 on success.
+ *       (float32) to OUT.  WINDOW > 0 runs the *_rect calls with that causal
+ *       window; FUSED = 1 replaces fa_bwd_dkdv and fa_bwd_dq by
+ *       fa_bwd_fused with a workspace of fa_bwd_fused_workspace_bytes.  Also
+ *       checks that an unsupported head dim is rejected before any launch.
+ *       Exit status 0 on success.
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,11 +58,12 @@ int main(int argc, char** argv) {
     printf("abi %d %s\n", fa_abi_version(), fa_status_str(FA_ERR_UNSUPPORTED));
     return fa_abi_version() == FA_ABI_VERSION ? 0 : 1;
   }
-  if (argc != 7) {
-    fprintf(stderr, "usage: %s --abi | IN OUT BH N D CAUSAL\n", argv[0]);
+  if (argc != 7 && argc != 9) {
+    fprintf(stderr, "usage: %s --abi | IN OUT BH N D CAUSAL [WINDOW FUSED]\n", argv[0]);
     return 1;
   }
   const int bh = atoi(argv[3]), n = atoi(argv[4]), d = atoi(argv[5]), causal = atoi(argv[6]);
+  const int window = argc == 9 ? atoi(argv[7]) : 0, fused = argc == 9 ? atoi(argv[8]) : 0;
   if (bh <= 0 || n <= 0 || d <= 0) return 1;
   const size_t elems = (size_t)bh * n * d, rows = (size_t)bh * n;
   const size_t tb = elems * sizeof(uint16_t), rb = rows * sizeof(float);
@@ -96,11 +100,27 @@ int main(int argc, char** argv) {
   }
 
   const float scale = 1.0f / sqrtf((float)d);
-  FA_OK_OR_FAIL(fa_fwd(q, k, v, o, lse, bh, n, d, FA_BF16, scale, causal, 0, 0, NULL));
+  if (window > 0)
+    FA_OK_OR_FAIL(fa_fwd_rect(q, k, v, o, lse, bh, n, n, d, FA_BF16, scale, causal, window, 0, 0, NULL));
+  else
+    FA_OK_OR_FAIL(fa_fwd(q, k, v, o, lse, bh, n, d, FA_BF16, scale, causal, 0, 0, NULL));
   FA_OK_OR_FAIL(fa_bwd_preprocess(o, dO, delta, bh, n, d, FA_BF16, NULL));
-  FA_OK_OR_FAIL(fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, bh, n, d, FA_BF16, scale, causal, 0, 0, NULL));
-  FA_OK_OR_FAIL(fa_bwd_dq(q, k, v, dO, lse, delta, dq, bh, n, d, FA_BF16, scale, causal, 0, 0, NULL));
+  void* ws = NULL;
+  if (fused) {
+    HIP_OK(hipMalloc(&ws, fa_bwd_fused_workspace_bytes(bh, n, d, FA_BF16)));
+    FA_OK_OR_FAIL(fa_bwd_fused(q, k, v, dO, lse, delta, dq, dk, dv, (float*)ws, bh, n, n, d, FA_BF16,
+                               scale, causal, window, 0, 0, NULL));
+  } else if (window > 0) {
+    FA_OK_OR_FAIL(fa_bwd_dkdv_rect(q, k, v, dO, lse, delta, dk, dv, bh, n, n, d, FA_BF16, scale, causal,
+                                   window, 0, 0, NULL));
+    FA_OK_OR_FAIL(fa_bwd_dq_rect(q, k, v, dO, lse, delta, dq, bh, n, n, d, FA_BF16, scale, causal,
+                                 window, 0, 0, NULL));
+  } else {
+    FA_OK_OR_FAIL(fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, bh, n, d, FA_BF16, scale, causal, 0, 0, NULL));
+    FA_OK_OR_FAIL(fa_bwd_dq(q, k, v, dO, lse, delta, dq, bh, n, d, FA_BF16, scale, causal, 0, 0, NULL));
+  }
   HIP_OK(hipDeviceSynchronize());
+  if (ws) HIP_OK(hipFree(ws));
 
   unsigned char* p = host_out;
   HIP_OK(hipMemcpy(p, o, tb, hipMemcpyDeviceToHost));
@@ -123,6 +143,6 @@ int main(int argc, char** argv) {
   for (size_t i = 0; i < sizeof(bufs) / sizeof(bufs[0]); ++i) HIP_OK(hipFree(bufs[i]));
   free(host_in);
   free(host_out);
-  printf("ok bh=%d n=%d d=%d causal=%d\n", bh, n, d, causal);
+  printf("ok bh=%d n=%d d=%d causal=%d window=%d fused=%d\n", bh, n, d, causal, window, fused);
   return 0;
 }
