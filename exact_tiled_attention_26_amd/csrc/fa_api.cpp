@@ -28,13 +28,13 @@ constexpr Bf16Tiling kBf16Tilings[] = {
     {kFused, 128, 64, 128}, {kFused, 64, 64, 128},
 };
 
-// float32 defaults per kernel (fwd, dkdv, dq, fused backward), measured at
-// 16 x 4096 x 64: 128-query tiles suit the forward and dQ kernels, dK/dV
-// keeps 64.
 // bf16 forward default at d = 128 when a sliding window is set (measured at
 // 32 x 8192 x 128: 16 % faster at a 256-key window, 8 % at 1024)
 constexpr Tiles kFwdWindowTiles = {128, 64};
 
+// float32 defaults per kernel (fwd, dkdv, dq, fused backward), measured at
+// 16 x 4096 x 64: 128-query tiles suit the forward and dQ kernels, dK/dV
+// keeps 64.
 constexpr Tiles kF32Defaults[] = {{128, 64}, {64, 64}, {128, 64}, {64, 64}};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -64,7 +64,8 @@
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every call
  *   only enqueues work on it and returns.  The caller orders
  *   fa_bwd_preprocess before fa_bwd_dkdv and fa_bwd_dq (which are
- *   independent of each other).
+ *   independent of each other) or before fa_bwd_fused.  Calls whose
+ *   outputs or workspace overlap must not run concurrently.
  * Empty input.  bh == 0 or n == 0 is a no-op that returns FA_OK (pointers
  *   are not touched and may be NULL).
  * Queries and keys of different lengths (the *_rect calls).  q, o, dO, dq
