@@ -133,6 +133,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         kf[kb][ds] = bf16x8{};
         vf[kb][ds] = bf16x8{};
       }
+      vf[kb][ds] = neg_bf16(vf[kb][ds]);   // see the dP accumulators below
     }
   }
 
@@ -237,20 +238,16 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   constexpr int PF = 3;                          // operand prefetch distance (groups)
 
   struct EwState {
-    float l2[2][4], dd[2][4];
+    float l2[2][4];
     f32x4 pv[2][NKB], dsv[2][NKB];
   };
-  auto ew_begin = [&](const float* lt, const float* dt, int t, EwState& e) __attribute__((always_inline)) {
+  auto ew_begin = [&](const float* lt, int t, EwState& e) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int rl = 32 * t + 16 * h + 4 * g;     // first of this lane's 4 rows
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rl);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rl);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e.l2[h][i] = l4[i] * kLog2e;
-        e.dd[h][i] = d4[i];
-      }
+      for (int i = 0; i < 4; ++i) e.l2[h][i] = l4[i] * kLog2e;
     }
   };
   // item x = (h, i, kb) of step t
@@ -258,7 +255,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     const int kb = x % NKB, i = (x / NKB) % 4, h = x / (4 * NKB);
     const float p = exp2_fast(__builtin_fmaf(s[h][kb][i], scale_log2, -e.l2[h][i]));
     e.pv[h][kb][i] = p;
-    e.dsv[h][kb][i] = p * (dp[h][kb][i] - e.dd[h][i]);
+    e.dsv[h][kb][i] = p * dp[h][kb][i];   // = -dS (dp holds D - dP)
   };
   // Masked entries (key after query + off, or query past nq) get P = dS = 0.  Only
   // tiles crossing the diagonal or the end of the sequence run this, behind
@@ -311,14 +308,19 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       dk[u][kb] = mfma_bf16(aq, sb[kb], dk[u][kb]);
     }
   };
-  auto zero_acc = [&](Acc& s, Acc& dp) __attribute__((always_inline)) {
+  // S starts at zero; dP starts at D of its four rows, so that with V
+  // negated the products leave D - dP and the elementwise pass needs no
+  // subtraction (dS = P (dP - D) comes out negated; dK is scaled by -scale)
+  auto init_acc = [&](Acc& s, Acc& dp, const float* dt, int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + 32 * t + 16 * h + 4 * g);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[h][kb] = d4;
       }
+    }
   };
 
   // One query tile: the pipeline over its NQS steps.  The operand stream of a
@@ -331,7 +333,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     bf16x8 pbuf[2][NKB], sbuf[2][NKB];
     // prologue: G1(0) alone
     {
-      zero_acc(sa[0], pa[0]);
+      init_acc(sa[0], pa[0], dt, 0);
       bf16x8 rq[PF], ro[PF];
 #pragma unroll
       for (int u = 0; u < PF; ++u) g1_read(qt, ot, 0, u, rq[u], ro[u]);
@@ -349,8 +351,8 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       const bool has_g2 = t >= 1, has_g1 = t + 1 < NQS;
       const int ngroups = (has_g2 ? NG2 : 0) + (has_g1 ? NG1 : 0);
       EwState e;
-      ew_begin(lt, dt, t, e);
-      if (has_g1) zero_acc(sa[(t + 1) & 1], pa[(t + 1) & 1]);
+      ew_begin(lt, t, e);
+      if (has_g1) init_acc(sa[(t + 1) & 1], pa[(t + 1) & 1], dt, t + 1);
       // read group v of the region's operand stream
       auto read_v = [&](int v, bf16x8& aq, bf16x8& ao) __attribute__((always_inline)) {
         if (has_g2 && v < NG2) g2_read(qt, ot, t - 1, v, aq, ao);
@@ -427,7 +429,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     if (it + 1 < it1) tile_step(q_lds1, o_lds1, l_lds1, d_lds1, q_lds0, o_lds0, l_lds0, d_lds0, it + 1);
   }
 
-  // write dK = scale * dK_acc and dV
+  // write dK = -scale * dK_acc (the accumulator holds -dK / scale) and dV
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     const int key = k0w + 16 * kb + l16;
@@ -437,7 +439,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         bf16x4 k4, v4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          k4[i] = (__bf16)(dk[db][kb][i] * scale);
+          k4[i] = (__bf16)(dk[db][kb][i] * -scale);
           v4[i] = (__bf16)dv[db][kb][i];
         }
         *reinterpret_cast<bf16x4*>(dK + hoffk + (size_t)key * D + 16 * db + 4 * g) = k4;
@@ -503,6 +505,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         qf[qb][ds] = bf16x8{};
         of[qb][ds] = bf16x8{};
       }
+      of[qb][ds] = neg_bf16(of[qb][ds]);   // see the dP^T accumulators below
     }
     l2q[qb] = (row < nq) ? LSE[(size_t)head * nq + row] * kLog2e : __builtin_inff();
     dq_d[qb] = (row < nq) ? DELTA[(size_t)head * nq + row] : 0.f;
@@ -528,14 +531,17 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     const bool active = !CAUSAL || (j0 <= q0w + QW - 1 + off && (!BAND || j0 + BC - 1 > q0w + lo));
     if (active) {
-      // S^T = K Q^T, dP^T = V dO^T: lane holds key 16kb + 4g + i, query 16qb + l16
+      // S^T = K Q^T, dP^T = V dO^T: lane holds key 16kb + 4g + i, query 16qb + l16.
+      // dP^T starts at D of the lane's query and dO is negated, so the
+      // products leave D - dP and the elementwise pass needs no subtraction
+      // (dS = P (dP - D) comes out negated; dQ is scaled by -scale).
       f32x4 s[NKB][NQB], dp[NKB][NQB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[kb][qb] = f32x4{dq_d[qb], dq_d[qb], dq_d[qb], dq_d[qb]};
         }
       // operands are read PF steps ahead of the MFMAs that use them; the
       // scheduling fences keep each read where it was issued, so LDS latency
@@ -572,7 +578,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = exp2_fast(__builtin_fmaf(s[kb][qb][i], scale_log2, -l2q[qb]));
-            dp[kb][qb][i] = p * (dp[kb][qb][i] - dq_d[qb]);
+            dp[kb][qb][i] = p * dp[kb][qb][i];   // = -dS
           }
       // masked entries get dS = 0; only tiles crossing the diagonal or the end
       // of the sequence run this, behind a uniform branch
@@ -634,7 +640,7 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int db = 0; db < NDB; ++db) {
         bf16x4 q4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q4[i] = (__bf16)(acc[db][qb][i] * scale);
+        for (int i = 0; i < 4; ++i) q4[i] = (__bf16)(acc[db][qb][i] * -scale);   // acc holds -dQ / scale
         *reinterpret_cast<bf16x4*>(dQ + hoffq + (size_t)row * D + 16 * db + 4 * g) = q4;
       }
     }
@@ -696,7 +702,7 @@ hipError_t launch_bwd_fused_bf16(const void* q, const void* k, const void* v, co
   if (e != hipSuccess) return e;
   const size_t blocks = std::min<size_t>((n / 4 + 255) / 256, 8192);
   hipLaunchKernelGGL(dq_from_acc_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dq_acc, (__bf16*)dq,
-                     n / 4, scale);
+                     n / 4, -scale);   // the fused dK/dV kernel accumulates -dQ / scale
   return hipGetLastError();
 }
 

@@ -95,6 +95,12 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {
   return r;
 }
 
+// -x of eight bf16 values (sign bits flipped: exact)
+__device__ __forceinline__ bf16x8 neg_bf16(const bf16x8& x) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x) ^ 0x80008000u;
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 __device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
