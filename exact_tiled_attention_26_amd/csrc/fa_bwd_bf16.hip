@@ -112,6 +112,18 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     if (wave == 0) rows_load_async<BR>(ld, Lh, i0, nq, lane);
     if (wave == 1) rows_load_async<BR>(dd, Dh, i0, nq, lane);
   };
+  // L of the rows is turned to base 2 (times log2 e) in LDS once per row,
+  // instead of once per lane and step: wave 0, whose copy it is, rescales
+  // it in place once the copy has landed, before the barrier that publishes
+  // the tile.  (Not with a window: there the compiler's register allocation
+  // of the changed step spills; that variant keeps the per-step product.)
+  constexpr bool L2_IN_LDS = !BAND;
+  auto scale_l = [&](float* ld) __attribute__((always_inline)) {
+    if (L2_IN_LDS && wave == 0) {
+#pragma unroll
+      for (int k = 0; k < BR / 64; ++k) ld[64 * k + lane] *= kLog2e;
+    }
+  };
   if constexpr (FUSED) {
     const AsyncTileCopy<D, BC, NW, false> kcopier(wave, lane);
     kcopier.issue(kt_lds, K + hoffk + (size_t)k0 * D, nk - k0);
@@ -150,6 +162,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const NatReader<D> nat(l16, g);
   const TrReader<D> tr(l16, g);
   async_copy_wait();
+  scale_l(l_lds0);
   __syncthreads();
   if constexpr (FUSED) {
     // K rows past nk were copied from row nk - 1: clear them so that those
@@ -247,7 +260,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       const int rl = 32 * t + 16 * h + 4 * g;     // first of this lane's 4 rows
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rl);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e.l2[h][i] = l4[i] * kLog2e;
+      for (int i = 0; i < 4; ++i) e.l2[h][i] = L2_IN_LDS ? l4[i] : l4[i] * kLog2e;
     }
   };
   // item x = (h, i, kb) of step t
@@ -420,6 +433,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       }
     }
     async_copy_wait();
+    if (it + 1 < it1) scale_l(ln);
     __syncthreads();
   };
 
