@@ -40,7 +40,11 @@
 namespace fa {
 
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kFwdBuffers = 2;   // LDS buffers per operand (copy distance NBUF - 1 tiles)
+// LDS buffers per operand: 4 (steps in pairs, one barrier per pair) where
+// the 4 x 2 tiles still leave room for the workgroups a CU can hold, else 2
+// (d = 128 with four waves: 128 KB would allow one workgroup per CU)
+template <int D, int NW>
+constexpr int fwd_buffers() { return (D == 128 && NW == 4) ? 2 : 4; }
 
 // nq query rows attend to nk key rows; causal masking is aligned to the end
 // of the key sequence (query i sees keys 0 .. i + nk - nq), and a window > 0
@@ -64,7 +68,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   constexpr int NE = NKB * NQB * 4;   // probabilities per lane per tile
   static_assert(US == UP, "the two products of a tile are interleaved step by step");
   static_assert(NKS == 2, "probabilities are produced in two halves, one per PV half");
-  static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
+  static_assert(NBUF == 2 || NBUF == 3 || NBUF == 4, "double, triple or pairwise buffering");
   static_assert(!BAND || CAUSAL, "a window narrows causal attention");
 
   // NBUF LDS buffers per operand; K runs one tile ahead of V, and every copy
@@ -215,6 +219,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   };
 
   // prologue: scores of the first key tile and the first exponent base
+  if constexpr (NBUF == 4) {
+    // pairs of steps share one barrier: steps 0 and 1 also need K(2), V(1)
+    if (jt0 + 2 < ntk) copier.issue_at(kbase + 2 * TB, Kh + (size_t)(jt0 + 2) * BC * D, nk - (jt0 + 2) * BC);
+    if (jt0 + 1 < ntk) copier.issue_at(vbase + TB, Vh + (size_t)(jt0 + 1) * BC * D, nk - (jt0 + 1) * BC);
+  }
   async_copy_wait();
   // copies that step 0 waits for when the distance is two steps
   if constexpr (NBUF == 3) {
@@ -330,13 +339,29 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // this wave has rows that see tile t (with a window, only the scores of
   // tile t+1 in the step before the wave's first tile), then wait for the
   // copies that step t+1 needs and synchronise.
+  // NBUF = 4: steps go in pairs (t, t+1) with one barrier after the pair.
+  // K(t+1), K(t+2), V(t), V(t+1) are resident when the pair starts; its first
+  // step copies the next pair's K(t+3), K(t+4), V(t+2), V(t+3) into the
+  // buffers the previous pair finished with.  ph = (t - jt0) mod 4, a
+  // compile-time constant, so every buffer address is one.
   constexpr int PER = AsyncTileCopy<D, BC, NW>::PER_WAVE;   // copy instructions per tile and wave
-  auto step = [&](f32x4 (&sc)[NKB][NQB], f32x4 (&sn)[NKB][NQB], int t) __attribute__((always_inline)) {
-    const int r = t - jt0;
+  auto step = [&](f32x4 (&sc)[NKB][NQB], f32x4 (&sn)[NKB][NQB], int t, auto ph) __attribute__((always_inline)) {
+    const int r = NBUF == 4 ? decltype(ph)::value : t - jt0;
     const int b0 = r % NBUF, b1 = (r + 1) % NBUF, bl = (r + NBUF - 1) % NBUF;
     const bool ck = t + NBUF < ntk, cv = t + NBUF - 1 < ntk;
-    if (cv) copier.issue_at(vbase + bl * TB, Vh + (size_t)(t + NBUF - 1) * BC * D, nk - (t + NBUF - 1) * BC);
-    if (ck) copier.issue_at(kbase + b0 * TB, Kh + (size_t)(t + NBUF) * BC * D, nk - (t + NBUF) * BC);
+    if constexpr (NBUF == 4) {
+      if (r % 2 == 0) {
+        if (t + 2 < ntk) copier.issue_at(vbase + ((r + 2) % 4) * TB, Vh + (size_t)(t + 2) * BC * D, nk - (t + 2) * BC);
+        if (t + 3 < ntk) {
+          copier.issue_at(kbase + ((r + 3) % 4) * TB, Kh + (size_t)(t + 3) * BC * D, nk - (t + 3) * BC);
+          copier.issue_at(vbase + ((r + 3) % 4) * TB, Vh + (size_t)(t + 3) * BC * D, nk - (t + 3) * BC);
+        }
+        if (t + 4 < ntk) copier.issue_at(kbase + b0 * TB, Kh + (size_t)(t + 4) * BC * D, nk - (t + 4) * BC);
+      }
+    } else {
+      if (cv) copier.issue_at(vbase + bl * TB, Vh + (size_t)(t + NBUF - 1) * BC * D, nk - (t + NBUF - 1) * BC);
+      if (ck) copier.issue_at(kbase + b0 * TB, Kh + (size_t)(t + NBUF) * BC * D, nk - (t + NBUF) * BC);
+    }
     if (t <= last && (!BAND || t >= first)) {
       const __bf16* kn = k_lds[b1];
       const __bf16* vt = v_lds[b0];
@@ -352,20 +377,41 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     } else if constexpr (BAND) {
       if (t + 1 == first && first <= last) scores_only(sn, k_lds[b1], t + 1);
     }
-    if constexpr (NBUF == 3) {
-      if (ck) async_copy_wait_allbut<2 * PER>();
-      else if (cv) async_copy_wait_allbut<PER>();
-      else async_copy_wait();
+    if constexpr (NBUF == 4) {
+      if (r % 2 == 1 || t + 1 >= ntk) {
+        async_copy_wait();
+        __syncthreads();
+      }
     } else {
-      async_copy_wait();
+      if constexpr (NBUF == 3) {
+        if (ck) async_copy_wait_allbut<2 * PER>();
+        else if (cv) async_copy_wait_allbut<PER>();
+        else async_copy_wait();
+      } else {
+        async_copy_wait();
+      }
+      __syncthreads();
     }
-    __syncthreads();
   };
 
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if constexpr (NBUF == 4) {
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
 #pragma unroll 1
-  for (int t = jt0; t < ntk; t += 2) {
-    step(sa, sb, t);
-    if (t + 1 < ntk) step(sb, sa, t + 1);
+    for (int t = jt0; t < ntk; t += 4) {
+      step(sa, sb, t, P0{});
+      if (t + 1 < ntk) step(sb, sa, t + 1, P1{});
+      if (t + 2 < ntk) step(sa, sb, t + 2, P2{});
+      if (t + 3 < ntk) step(sb, sa, t + 3, P3{});
+    }
+  } else {
+#pragma unroll 1
+    for (int t = jt0; t < ntk; t += 2) {
+      step(sa, sb, t, P0{});
+      if (t + 1 < ntk) step(sb, sa, t + 1, P1{});
+    }
   }
 
   // epilogue: O = acc / l, L = (m + log2 l) * ln 2
@@ -396,10 +442,11 @@ static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, v
   const int ntq = (nq + BR - 1) / BR;
   const dim3 grid((unsigned)(ntq * bh)), block(NW * 64);
   const float sl2 = scale * kLog2e;
-  auto kern = (causal && window > 0) ? fwd_bf16_kernel<D, QW, NW, BC, true, true, true, kFwdBuffers>
-            : causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true, false, kFwdBuffers>
-            : (nk % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, false, kFwdBuffers>
-                       : fwd_bf16_kernel<D, QW, NW, BC, false, false, false, kFwdBuffers>;
+  constexpr int NB = fwd_buffers<D, NW>();
+  auto kern = (causal && window > 0) ? fwd_bf16_kernel<D, QW, NW, BC, true, true, true, NB>
+            : causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true, false, NB>
+            : (nk % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, false, NB>
+                       : fwd_bf16_kernel<D, QW, NW, BC, false, false, false, NB>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                      (__bf16*)o, lse, bh, nq, nk, window, sl2);
   return hipGetLastError();
