@@ -17,7 +17,9 @@
 //   operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
 // * Key/value tiles of BC rows go from HBM straight into swizzled,
 //   double-buffered LDS tiles with global_load_lds (no staging registers);
-//   the copy of tile j+1 runs while tile j is computed, one barrier per tile.
+//   the copy of tile j+1 runs while tile j is computed, one barrier per tile
+//   -- or, with four buffers per operand, tiles go in pairs: the next pair
+//   is copied while one pair is computed, one barrier per pair.
 // * Scores are kept transposed (keys x queries) so that each lane owns one
 //   query column: the row max is in-lane max operations plus two cross-lane
 //   steps, and the accumulator layout of S^T is directly the B operand of
