@@ -465,7 +465,9 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
 // Occupancy: with 32-key tiles the kernel fits two waves per SIMD (at most
 // 256 registers each), so the matrix products of one wave overlap the
-// element-wise work of the other; with 64-key tiles it holds one.
+// element-wise work of the other; with 64-key tiles it holds one.  Eight
+// waves (256 query rows) share each K/V tile copy at d = 128: measured
+// 1.5 % faster causal and 3 % non-causal than four at 32 x 8192 x 128.
 template <int D, int QW, int NW, int BC, bool CAUSAL, bool BAND>
 __global__ __launch_bounds__(NW * 64, BC == 32 ? 2 : 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -758,6 +760,8 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
                           hipStream_t st) {
   if (d == 128 && bm == 128 && bn == 32)
     return launch_dq_inst<128, 32, 4, 32>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
+  if (d == 128 && bm == 256 && bn == 32)
+    return launch_dq_inst<128, 32, 8, 32>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   if (d == 128 && bm == 128 && bn == 64)
     return launch_dq_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   if (d == 64 && bm == 128 && bn == 32)

@@ -55,7 +55,7 @@ def test_version_and_strings(lib):
 def test_default_tiles(lib):
     assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_FWD) == (256, 64)
     assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_DKDV) == (128, 128)
-    assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_DQ) == (128, 32)
+    assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_DQ) == (256, 32)
     assert fa.fa_default_tiles(fa.FA_F32, 16, fa.KERNEL_FWD) == (128, 64)
     assert fa.fa_default_tiles(fa.FA_F32, 64, fa.KERNEL_DKDV) == (64, 64)
     assert fa.fa_default_tiles(fa.FA_F32, 128, fa.KERNEL_DQ) == (128, 64)

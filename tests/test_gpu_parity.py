@@ -132,8 +132,9 @@ def test_bf16_2048_d64_noncausal(dq_tiles):
 
 
 # every bf16 d = 128 tiling: forward (128, 64) and (256, 64), dK/dV (64, 128)
-# and (128, 128), dQ (128, 32) and (128, 64)
-BF16_D128_TILINGS = [((128, 64), (64, 128), (128, 32)), ((256, 64), (128, 128), (128, 64))]
+# and (128, 128), dQ (256, 32), (128, 32) and (128, 64)
+BF16_D128_TILINGS = [((128, 64), (64, 128), (128, 32)), ((256, 64), (128, 128), (128, 64)),
+                     ((256, 64), (128, 128), (256, 32))]
 
 
 @pytest.mark.parametrize("causal", [False, True])
