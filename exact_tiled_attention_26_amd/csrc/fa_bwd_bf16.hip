@@ -20,6 +20,12 @@
 // * dQ: a workgroup owns BR = NW * QW queries; wave w keeps its Q and dO rows
 //   in registers.  Key tiles of K and V are staged through LDS.  S^T and dP^T
 //   (keys x queries) feed dQ^T += K^T dS^T with K^T read transposed from LDS.
+// * Eq 17's subtraction is folded into the products: each dP accumulator
+//   starts at D of its rows and the operand that multiplies into dP (V in
+//   dK/dV, dO in dQ) is negated once when loaded (exact in bf16), so the
+//   products leave D - dP and one multiply gives -dS = P (D - dP).  The dK
+//   and dQ accumulators therefore hold -dK / scale and -dQ / scale, and the
+//   epilogues multiply by -scale.
 // * Causal mode visits only the tiles that hold a visible (query, key) pair
 //   and masks only tiles crossing the diagonal; a sliding window (BAND
 //   instances) also bounds the loops from the band's other edge.  Workgroups
