@@ -23,7 +23,7 @@ struct Bf16Tiling { int kernel, d, bm, bn; };
 constexpr Bf16Tiling kBf16Tilings[] = {
     {kFwd, 128, 256, 64},  {kFwd, 128, 128, 64},
     {kFwd, 64, 128, 64},   {kFwd, 64, 256, 64},
-    {kDkdv, 128, 128, 128}, {kDkdv, 128, 64, 128}, {kDkdv, 64, 64, 128},
+    {kDkdv, 128, 128, 128}, {kDkdv, 128, 64, 128}, {kDkdv, 64, 128, 128}, {kDkdv, 64, 64, 128},
     {kDq, 128, 256, 32},   {kDq, 128, 128, 32},   {kDq, 128, 128, 64},   {kDq, 64, 128, 64},   {kDq, 64, 128, 32},
     {kFused, 128, 64, 128}, {kFused, 64, 64, 128},
 };

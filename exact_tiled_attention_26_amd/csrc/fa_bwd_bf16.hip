@@ -756,6 +756,8 @@ hipError_t launch_dkdv_bf16(const void* q, const void* k, const void* v, const v
     return launch_dkdv_inst<128, 32, 4, 128>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, window, st);
   if (d == 64 && bm == 64 && bn == 128)
     return launch_dkdv_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, window, st);
+  if (d == 64 && bm == 128 && bn == 128)
+    return launch_dkdv_inst<64, 32, 4, 128>(q, k, v, dO, lse, delta, dk, dv, bh, nq, nk, scale, causal, window, st);
   return hipErrorInvalidValue;
 }
 

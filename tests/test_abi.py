@@ -55,6 +55,7 @@ def test_version_and_strings(lib):
 def test_default_tiles(lib):
     assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_FWD) == (256, 64)
     assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_DKDV) == (128, 128)
+    assert fa.fa_default_tiles(fa.FA_BF16, 64, fa.KERNEL_DKDV) == (128, 128)
     assert fa.fa_default_tiles(fa.FA_BF16, 128, fa.KERNEL_DQ) == (256, 32)
     assert fa.fa_default_tiles(fa.FA_F32, 16, fa.KERNEL_FWD) == (128, 64)
     assert fa.fa_default_tiles(fa.FA_F32, 64, fa.KERNEL_DKDV) == (64, 64)
@@ -133,7 +134,8 @@ def test_scale_must_be_finite_positive(lib):
 def test_tilings(lib):
     # bf16: only the tuned tilings
     assert fwd(lib, bm=64, bn=64, q=0) == fa.FA_ERR_UNSUPPORTED    # tiling is checked before pointers
-    assert dkdv(lib, bm=128, bn=128, q=0) == fa.FA_ERR_UNSUPPORTED
+    assert dkdv(lib, bm=256, bn=128, q=0) == fa.FA_ERR_UNSUPPORTED
+    assert dkdv(lib, bm=128, bn=128, q=0) == fa.FA_ERR_INVALID_ARG   # d = 64 has it; then null q
     assert dq(lib, bm=16, bn=16, q=0) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, bm=-1, bn=0) == fa.FA_ERR_INVALID_ARG
     # float32: block_m in {16,32,64,128}, block_n multiple of 4 up to 128, LDS budget

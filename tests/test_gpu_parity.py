@@ -113,15 +113,16 @@ def test_tile_sweep(causal):
             assert np.abs(g[name] - results[0][name]).max() <= 1e-5 * scale, name
 
 
-# every bf16 d = 64 tiling: forward (128, 64) and (256, 64), dK/dV (64, 128),
-# dQ (128, 64) and (128, 32)
-@pytest.mark.parametrize("fwd_tiles,dq_tiles", [((128, 64), (128, 64)), ((256, 64), (128, 32))])
-def test_bf16_2048_d64_causal(fwd_tiles, dq_tiles):
+# every bf16 d = 64 tiling: forward (128, 64) and (256, 64), dK/dV (128, 128)
+# and (64, 128), dQ (128, 64) and (128, 32)
+@pytest.mark.parametrize("fwd_tiles,dkdv_tiles,dq_tiles", [((128, 64), (128, 128), (128, 64)),
+                                                           ((256, 64), (64, 128), (128, 32))])
+def test_bf16_2048_d64_causal(fwd_tiles, dkdv_tiles, dq_tiles):
     """batch 4 x heads 8, N = 2048, d = 64, bf16, causal."""
     w = WORKLOADS["bf16_2048_d64"]
     arrays = make_inputs(w.bh, w.n, w.d, seed=0)
-    g = run_gpu(arrays, "bf16", True, fwd_tiles, (0, 0), dq_tiles)
-    compare_full(g, "bf16", True, label=f"bf16 32x2048x64 fwd{fwd_tiles} dq{dq_tiles}")
+    g = run_gpu(arrays, "bf16", True, fwd_tiles, dkdv_tiles, dq_tiles)
+    compare_full(g, "bf16", True, label=f"bf16 32x2048x64 fwd{fwd_tiles} dkdv{dkdv_tiles} dq{dq_tiles}")
 
 
 @pytest.mark.parametrize("dq_tiles", [(128, 64), (128, 32)])
