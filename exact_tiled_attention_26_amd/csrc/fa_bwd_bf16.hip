@@ -774,6 +774,8 @@ hipError_t launch_dq_bf16(const void* q, const void* k, const void* v, const voi
     return launch_dq_inst<128, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   if (d == 64 && bm == 128 && bn == 32)
     return launch_dq_inst<64, 32, 4, 32>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
+  if (d == 64 && bm == 256 && bn == 64)
+    return launch_dq_inst<64, 32, 8, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   if (d == 64 && bm == 128 && bn == 64)
     return launch_dq_inst<64, 32, 4, 64>(q, k, v, dO, lse, delta, dq, bh, nq, nk, scale, causal, window, st);
   return hipErrorInvalidValue;

@@ -125,7 +125,7 @@ def test_bf16_2048_d64_causal(fwd_tiles, dkdv_tiles, dq_tiles):
     compare_full(g, "bf16", True, label=f"bf16 32x2048x64 fwd{fwd_tiles} dkdv{dkdv_tiles} dq{dq_tiles}")
 
 
-@pytest.mark.parametrize("dq_tiles", [(128, 64), (128, 32)])
+@pytest.mark.parametrize("dq_tiles", [(0, 0), (128, 64), (128, 32), (256, 64)])
 def test_bf16_2048_d64_noncausal(dq_tiles):
     arrays = make_inputs(8, 2048, 64, seed=1)
     g = run_gpu(arrays, "bf16", False, (0, 0), (0, 0), dq_tiles)

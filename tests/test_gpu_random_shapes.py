@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"fp32": dict(o=1e-5, lse=1e-5, grad=1e-4), "bf16": dict(o=1e-2, lse=1e-3, grad=3e-2)}
 BF16_TILES = {128: dict(fwd=[(256, 64), (128, 64)], dkdv=[(128, 128), (64, 128)], dq=[(256, 32), (128, 32), (128, 64)]),
-              64: dict(fwd=[(128, 64), (256, 64)], dkdv=[(128, 128), (64, 128)], dq=[(128, 64), (128, 32)])}
+              64: dict(fwd=[(128, 64), (256, 64)], dkdv=[(128, 128), (64, 128)], dq=[(128, 64), (128, 32), (256, 64)])}
 F32_TILES = [(16, 12), (32, 64), (64, 32), (128, 64), (64, 64), (16, 128)]
 
 
