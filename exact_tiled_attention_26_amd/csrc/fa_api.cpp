@@ -34,11 +34,6 @@ constexpr Tiles kFwdWindowTiles = {128, 64};
 // the same holds for dQ: four-wave, 128-query tiles with a window (at a
 // 256-key window 0.116 against 0.135 ms for the 256-query default)
 constexpr Tiles kDqWindowTiles = {128, 32};
-// bf16 dQ at d = 64 without the causal mask: eight-wave, 256-query tiles
-// (0.060 against 0.085 ms at 32 x 2048 x 64; the 128-query instance needs
-// more than 256 registers there and runs one wave per SIMD), while causal
-// keeps (128, 64) (0.048 against 0.053 ms)
-constexpr Tiles kDqD64FullTiles = {256, 64};
 
 // float32 defaults per kernel (fwd, dkdv, dq, fused backward), measured at
 // 16 x 4096 x 64: 128-query tiles suit the forward and dQ kernels, dK/dV
@@ -248,10 +243,6 @@ fa_status fa_bwd_dq_rect(const void* q, const void* k, const void* v, const void
   if (default_tiles && window > 0 && dtype == FA_BF16 && d == 128) {
     block_m = kDqWindowTiles.bm;
     block_n = kDqWindowTiles.bn;
-  }
-  if (default_tiles && !causal && dtype == FA_BF16 && d == 64) {
-    block_m = kDqD64FullTiles.bm;
-    block_n = kDqD64FullTiles.bn;
   }
   if ((s = check_grid(bh, nq, block_m)) != FA_OK) return s;
   if ((s = check_ptrs(q, k, v, dO, lse, delta, dq)) != FA_OK) return s;

@@ -471,11 +471,13 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
 // Occupancy: with 32-key tiles the kernel fits two waves per SIMD (at most
 // 256 registers each), so the matrix products of one wave overlap the
-// element-wise work of the other; with 64-key tiles it holds one.  Eight
+// element-wise work of the other; with 64-key tiles it holds one at d = 128
+// and two at d = 64 (asked for: left free, the compiler takes up to 262
+// registers there, and two waves measured 9 % faster causal).  Eight
 // waves (256 query rows) share each K/V tile copy at d = 128: measured
 // 1.5 % faster causal and 3 % non-causal than four at 32 x 8192 x 128.
 template <int D, int QW, int NW, int BC, bool CAUSAL, bool BAND>
-__global__ __launch_bounds__(NW * 64, BC == 32 ? 2 : 1)
+__global__ __launch_bounds__(NW * 64, (BC == 32 || D == 64) ? 2 : 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                     const float* __restrict__ LSE, const float* __restrict__ DELTA,

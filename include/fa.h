@@ -140,9 +140,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
  * window < 0, or window > 0 without causal, is FA_ERR_INVALID_ARG.  With a
  * window (narrower than nk) and block_m = block_n = 0, the bf16 forward at
  * d = 128 uses the (128, 64) tiling instead of fa_default_tiles' (256, 64),
- * and fa_bwd_dq_rect at d = 128 the (128, 32) tiling instead of (256, 32).
- * Without the causal mask and with block_m = block_n = 0, fa_bwd_dq_rect
- * at d = 64 (bf16) uses (256, 64) instead of (128, 64). */
+ * and fa_bwd_dq_rect at d = 128 the (128, 32) tiling instead of (256, 32). */
 fa_status fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
                       int bh, int nq, int nk, int d, fa_dtype dtype, float scale, int causal,
                       int window, int block_m, int block_n, void* stream);
