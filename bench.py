@@ -159,9 +159,18 @@ def rocprof_summary(paths):
             "select name, count(*), avg(end - start), min(end - start), max(end - start) "
             "from kernels group by name order by sum(end - start) desc").fetchall()
         if rows:
-            print(f"{'calls':>5} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel")
+            # last_us: mean of the last `timed` dispatches of the kernel (a
+            # default bench.py run times its last 20 steps, one dispatch each)
+            timed = 20
+            print(f"{'calls':>5} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'median_us':>10} "
+                  f"{'last_us':>10}  kernel (last_us: mean of the last {timed} dispatches)")
             for name, cnt, avg, mn, mx in rows:
-                print(f"{cnt:5d} {avg / 1e3:10.1f} {mn / 1e3:10.1f} {mx / 1e3:10.1f}  {name[:100]}")
+                ds = [r[0] for r in con.execute(
+                    "select end - start from kernels where name = ? order by start", (name,))]
+                med = sorted(ds)[len(ds) // 2]
+                last = ds[-timed:]
+                print(f"{cnt:5d} {avg / 1e3:10.1f} {mn / 1e3:10.1f} {mx / 1e3:10.1f} {med / 1e3:10.1f} "
+                      f"{sum(last) / len(last) / 1e3:10.1f}  {name[:100]}")
         try:
             pm = con.execute("select name, counter_name, avg(counter_value), count(*) from pmc_events "
                              "group by name, counter_name order by name").fetchall()
