@@ -260,6 +260,13 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       if (r % 8 == 7) pb[h][qb] = pack_bf16(sc[2 * h][qb], sc[2 * h + 1][qb]);
     };
     constexpr int EA = 3 * NE / 4;   // items done in phase A
+    // The two waves of a SIMD run the same pipeline; issue priority is
+    // raised for the score products and most of the probabilities (phase A)
+    // and dropped for the PV products (phase B), so that a wave in phase A
+    // gets the issue slots when the other is in phase B and the two drift
+    // into complementary phases (measured 1.5 % faster than equal priority;
+    // the opposite assignment measured no change).
+    __builtin_amdgcn_s_setprio(1);
     // phase A
     {
       constexpr int PF = 3;
@@ -287,6 +294,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // phase B
     {
       constexpr int PF = 3;
