@@ -26,7 +26,6 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
 MFMA_FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
-METRIC = "fwd+bwd attention TFLOPS (bf16, causal, N=8192, d=128) + % of MFMA peak"
 
 
 def score_pairs(n, causal, window=0):
@@ -108,43 +107,88 @@ def measured_traffic(kernel):
     return None
 
 
-def cpu_baseline(bh, n, d, causal, budget_s=25.0, window=0):
-    """The fp64 oracle timed on host cores on a bounded sample of the same
-    workload: whole heads (forward + backward) until about `budget_s`."""
-    import numpy as np
-
+def _oracle_seconds(q, k, v, do, causal, window):
+    """Wall seconds of the oracle's forward and backward on one head."""
     import oracle
-    from workloads import cast_io, make_inputs, to_f64
-
-    cores = len(os.sched_getaffinity(0))
-    rng_inputs = make_inputs(1, n, d, seed=0)
-    q, k, v, do = (to_f64(t)[0] for t in cast_io(rng_inputs, "bf16"))
-    heads = 0
     t0 = time.perf_counter()
-    while True:
-        oracle.attention_forward(q, k, v, causal=causal, window=window)
-        oracle.attention_backward(q, k, v, do, causal=causal, window=window)
-        heads += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or el / heads * (heads + 1) > budget_s * 1.5:
-            break
-    fwd, bwd = counted_flops(heads, n, d, causal, window)
-    threads = None
+    oracle.attention_forward(q, k, v, causal=causal, window=window)
+    t1 = time.perf_counter()
+    oracle.attention_backward(q, k, v, do, causal=causal, window=window)
+    return t1 - t0, time.perf_counter() - t1
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+        return max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
     except Exception:
-        pass
-    return {
-        "value": (fwd + bwd) / el / 1e12,
+        return None
+
+
+def cpu_oracle_run(name, causal, heads=None, window=0, budget_s=None):
+    """The fp64 oracle (as it stands) timed on the host, forward and backward
+    separately, one head after another on the workload's own seeded inputs:
+    every head, the first `heads` heads, or heads until about `budget_s`."""
+    from workloads import WORKLOADS, cast_io, make_inputs, to_f64
+
+    w = WORKLOADS[name]
+    arrays = make_inputs(w.bh, w.n, w.d, seed=0)
+    q, k, v, do = (to_f64(t) for t in cast_io(arrays, w.dtype))
+    todo = w.bh if heads is None else min(heads, w.bh)
+    fwd_s = bwd_s = 0.0
+    done = 0
+    for h in range(todo):
+        a, b = _oracle_seconds(q[h], k[h], v[h], do[h], causal, window)
+        fwd_s, bwd_s, done = fwd_s + a, bwd_s + b, done + 1
+        el = fwd_s + bwd_s
+        if budget_s is not None and (el >= budget_s or el / done * (done + 1) > budget_s * 1.5):
+            break
+    fwd_fl, bwd_fl = counted_flops(done, w.n, w.d, causal, window)
+    return {"workload": name, "batch_heads": w.bh, "seq_len": w.n, "head_dim": w.d, "dtype": w.dtype,
+            "causal": causal, "heads_timed": done, "fwd_s": round(fwd_s, 3), "bwd_s": round(bwd_s, 3),
+            "fwd_tflops": fwd_fl / fwd_s / 1e12, "bwd_tflops": bwd_fl / bwd_s / 1e12,
+            "tflops": (fwd_fl + bwd_fl) / (fwd_s + bwd_s) / 1e12}
+
+
+# the oracle timed per configuration: every head of the first four, two heads
+# of the long-context one
+CPU_ORACLE_CONFIGS = (("gradcheck_48", (False, True), None), ("tile_sweep_256", (False, True), None),
+                      ("bf16_2048_d64", (True,), None), ("headline_8192_d128", (True, False), None),
+                      ("long_32768_d128", (True,), 2))
+
+
+def cpu_baseline(w, causal, window=0, scope="all", budget_s=25.0):
+    """The contract's cpu_baseline object (the oracle on the timed workload)
+    and, with scope "all", the per-configuration oracle table."""
+    cores = len(os.sched_getaffinity(0))
+    threads = _blas_threads() or cores
+    table = []
+    main = None
+    if scope == "all":
+        for name, modes, heads in CPU_ORACLE_CONFIGS:
+            for c in modes:
+                print(f"# oracle: {name} causal={c}", file=sys.stderr, flush=True)
+                r = cpu_oracle_run(name, c, heads)
+                table.append(r)
+                if name == w.name and c == causal and not window:
+                    main = r
+    if main is None:
+        print(f"# oracle: {w.name} causal={causal} window={window} (sample)", file=sys.stderr, flush=True)
+        main = cpu_oracle_run(w.name, causal, window=window, budget_s=budget_s)
+    base = {
+        "value": main["tflops"],
         "unit": "TFLOPS",
-        "cores": threads or cores,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{heads} of {bh} heads (N={n}, d={d}, {'causal' if causal else 'non-causal'}"
-                  f"{f', window {window}' if window else ''}), "
-                  f"fp64 fwd+bwd, {el:.1f} s; host cores available: {cores}",
-        "seconds": el,
+        "sample": f"{main['heads_timed']} of {w.bh} heads (N={w.n}, d={w.d}, "
+                  f"{'causal' if causal else 'non-causal'}{f', window {window}' if window else ''}), "
+                  f"fp64 forward {main['fwd_s']:.1f} s + backward {main['bwd_s']:.1f} s; "
+                  f"host cores available: {cores}, BLAS threads: {threads}",
+        "seconds": main["fwd_s"] + main["bwd_s"],
     }
+    if table:
+        base["by_config"] = [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()} for r in table]
+    return base
 
 
 def rocprof_summary(paths):
@@ -182,6 +226,162 @@ def rocprof_summary(paths):
                 print(f"{cn:>12} {val:14.1f} {cnt:10d}  {name[:100]}")
 
 
+def metric_name(dtype, causal, window, n, d):
+    mode = ("causal" + (f", window {window}" if window else "")) if causal else "non-causal"
+    return f"fwd+bwd attention TFLOPS ({dtype}, {mode}, N={n}, d={d}) + % of MFMA peak"
+
+
+def _stats(xs):
+    ys = sorted(xs)
+    return {"avg_ms": round(sum(xs) / len(xs), 4), "median_ms": round(ys[len(ys) // 2], 4), "min_ms": round(ys[0], 4)}
+
+
+def measure(fa, torch, w, causal, window, tiles, fused, steps, warmup):
+    """Time `steps` whole steps (forward, preprocess, dK/dV, dQ, or the fused
+    backward) on the workload's seeded inputs, after `warmup` untimed ones.
+    Returns the wall time per step and per-kernel HIP-event times; every
+    event is recorded on the stream the kernels are launched on."""
+    from workloads import cast_io, make_inputs
+
+    bh, n, d = w.bh, w.n, w.d
+    ft, kt, qt = tiles
+    q, k, v, do = cast_io(make_inputs(bh, n, d, seed=0), w.dtype, "cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((bh, n), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    names = ("fwd", "preprocess", "bwd_fused") if fused else ("fwd", "preprocess", "dkdv", "dq")
+    ws = None
+    if fused:
+        nbytes = fa.fa_bwd_fused_workspace_bytes(bh, n, d, fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda") if nbytes else None
+    if window:
+        calls = [lambda: fa.fa_fwd_rect(q, k, v, o, lse, causal, None, *ft, stream=sptr, window=window)]
+    else:
+        calls = [lambda: fa.fa_fwd(q, k, v, o, lse, causal, None, *ft, stream=sptr)]
+    calls.append(lambda: fa.fa_bwd_preprocess(o, do, delta, stream=sptr))
+    if fused:
+        calls.append(lambda: fa.fa_bwd_fused(q, k, v, do, lse, delta, dq, dk, dv, ws, causal, None, *kt,
+                                             stream=sptr, window=window))
+    elif window:
+        calls.append(lambda: fa.fa_bwd_dkdv_rect(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr,
+                                                 window=window))
+        calls.append(lambda: fa.fa_bwd_dq_rect(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr,
+                                               window=window))
+    else:
+        calls.append(lambda: fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr))
+        calls.append(lambda: fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr))
+
+    def step(ev=None):
+        for j, call in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            call()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel = {nm: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, nm in enumerate(names)}
+    return {"names": names, "ms_per_step": wall * 1e3 / steps,
+            "event_ms_per_step": sum(ev[0].elapsed_time(ev[len(names)]) for ev in events) / steps,
+            "per_kernel": per_kernel, "step": step}
+
+
+def summarize(w, causal, window, m, peak):
+    """TFLOPS and fractions of the MFMA peak for one measured workload."""
+    bh, n, d = w.bh, w.n, w.d
+    elt = 2 if w.dtype == "bf16" else 4
+    names = m["names"]
+    stats = {nm: _stats(m["per_kernel"][nm]) for nm in names}
+    fwd_fl, bwd_fl = counted_flops(bh, n, d, causal, window)
+    kfl = kernel_flops(bh, n, d, causal, window)
+    kby = kernel_bytes(bh, n, d, elt)
+    fwd_ms = stats["fwd"]["avg_ms"]
+    bwd_ms = sum(stats[nm]["avg_ms"] for nm in names if nm != "fwd")
+    kernels = {}
+    for nm in names:
+        ent = dict(stats[nm])
+        if nm in kfl:
+            tf = kfl[nm] / (ent["avg_ms"] * 1e-3) / 1e12
+            ent["tflops"] = round(tf, 1)
+            ent["frac_mfma_peak"] = round(tf / peak, 4)
+        ent["hbm_gbs"] = round(kby[nm] / (ent["avg_ms"] * 1e-3) / 1e9, 1)
+        kernels[nm] = ent
+    tflops = (fwd_fl + bwd_fl) / (m["ms_per_step"] * 1e-3) / 1e12
+    return {
+        "ms_per_step": round(m["ms_per_step"], 4),
+        "tflops": round(tflops, 2),
+        "pct_of_mfma_peak": round(100 * tflops / peak, 2),
+        "fwd_tflops": round(fwd_fl / (fwd_ms * 1e-3) / 1e12, 1),
+        "fwd_pct_of_peak": round(100 * fwd_fl / (fwd_ms * 1e-3) / 1e12 / peak, 2),
+        "bwd_tflops": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 1),
+        "bwd_pct_of_peak": round(100 * bwd_fl / (bwd_ms * 1e-3) / 1e12 / peak, 2),
+        "event_ms_per_step": round(m["event_ms_per_step"], 4),
+        "kernels": kernels,
+    }
+
+
+def sample_clock(step, seconds=1.0):
+    """Shader (GFX) clock while the timed step runs back to back for about
+    `seconds`: the mean over the GPU's XCDs of amdsmi's current_gfxclks,
+    sampled every 10 ms; the first 30 % of the run (clock ramp) is dropped.
+    Returns None where amdsmi is not available."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:   # no SMI library or no access: the field stays null
+        print(f"# clock sampling unavailable: {e!r}", file=sys.stderr, flush=True)
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                clks = [c for c in amdsmi.amdsmi_get_gpu_metrics_info(handle)["current_gfxclks"] if isinstance(c, int)]
+                if clks:
+                    samples.append((time.perf_counter(), sum(clks) / len(clks)))
+            except Exception:
+                pass
+            time.sleep(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    t1 = time.perf_counter()
+    kept = [c for t, c in samples if t >= t0 + 0.3 * (t1 - t0)]
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not kept:
+        return None
+    kept.sort()
+    return {"mhz_median": round(kept[len(kept) // 2], 1), "mhz_min": round(kept[0], 1), "mhz_max": round(kept[-1], 1),
+            "samples": len(kept), "source": "amdsmi current_gfxclks (mean over XCDs), sampled every 10 ms while "
+                                            "the timed step ran back to back for about 1 s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,7 +395,12 @@ def main():
                     help="time the single-kernel backward (fa_bwd_fused, atomic dQ) instead of "
                          "fa_bwd_dkdv + fa_bwd_dq")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-scope", choices=("all", "sample"), default="all",
+                    help="all: the oracle on every configuration (about two minutes); sample: on the timed "
+                         "workload only, about --cpu-budget seconds")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the non-causal headline and long-context sub-records and the clock sampling")
     ap.add_argument("--fwd-tiles", default="0,0")
     ap.add_argument("--dkdv-tiles", default="0,0")
     ap.add_argument("--dq-tiles", default="0,0")
@@ -218,7 +423,7 @@ def main():
     import torch
 
     import exact_tiled_attention_26_amd as fa
-    from workloads import WORKLOADS, cast_io, make_inputs
+    from workloads import WORKLOADS
 
     if args.calibrate_copy:
         nbytes = args.calibrate_copy << 20
@@ -235,96 +440,26 @@ def main():
     window = args.window
     if window and not causal:
         ap.error("--window needs causal attention")
-    bh, n, d = w.bh, w.n, w.d
-    elt = 2 if w.dtype == "bf16" else 4
-    ft = tuple(int(x) for x in args.fwd_tiles.split(","))
-    kt = tuple(int(x) for x in args.dkdv_tiles.split(","))
-    qt = tuple(int(x) for x in args.dq_tiles.split(","))
-    print(f"# workload {w.name}: bh={bh} n={n} d={d} {w.dtype} causal={causal} window={window}",
+    tiles = tuple(tuple(int(x) for x in a.split(",")) for a in (args.fwd_tiles, args.dkdv_tiles, args.dq_tiles))
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    default_run = (w.name == "headline_8192_d128" and causal and not window and not args.fused_bwd
+                   and tiles == ((0, 0), (0, 0), (0, 0)))
+    print(f"# workload {w.name}: bh={w.bh} n={w.n} d={w.d} {w.dtype} causal={causal} window={window}",
           file=sys.stderr, flush=True)
 
-    q, k, v, do = cast_io(make_inputs(bh, n, d, seed=0), w.dtype, "cuda")
-    o = torch.empty_like(q)
-    lse = torch.empty((bh, n), dtype=torch.float32, device="cuda")
-    delta = torch.empty_like(lse)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
+    m = measure(fa, torch, w, causal, window, tiles, args.fused_bwd, args.steps, args.warmup)
+    print(f"# timed {args.steps} steps", file=sys.stderr, flush=True)
+    res = summarize(w, causal, window, m, peak)
+    clock = None
+    if not args.no_extra:
+        clock = sample_clock(m["step"])
+    del m
+    torch.cuda.empty_cache()
 
-    names = ("fwd", "preprocess", "bwd_fused") if args.fused_bwd else ("fwd", "preprocess", "dkdv", "dq")
-    ws = None
-    if args.fused_bwd:
-        nbytes = fa.fa_bwd_fused_workspace_bytes(bh, n, d, fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32)
-        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda") if nbytes else None
-
-    if window:
-        def fwd_call():
-            fa.fa_fwd_rect(q, k, v, o, lse, causal, None, *ft, stream=sptr, window=window)
-
-        def dkdv_call():
-            fa.fa_bwd_dkdv_rect(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr,
-                                window=window)
-
-        def dq_call():
-            fa.fa_bwd_dq_rect(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr, window=window)
-    else:
-        def fwd_call():
-            fa.fa_fwd(q, k, v, o, lse, causal, None, *ft, stream=sptr)
-
-        def dkdv_call():
-            fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, causal, None, *kt, stream=sptr)
-
-        def dq_call():
-            fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, causal, None, *qt, stream=sptr)
-
-    def fused_call():
-        fa.fa_bwd_fused(q, k, v, do, lse, delta, dq, dk, dv, ws, causal, None, *kt, stream=sptr, window=window)
-
-    calls = [fwd_call, lambda: fa.fa_bwd_preprocess(o, do, delta, stream=sptr)]
-    calls += [fused_call] if args.fused_bwd else [dkdv_call, dq_call]
-
-    def step(ev=None):
-        for j, call in enumerate(calls):
-            if ev is not None:
-                ev[j].record(stream)
-            call()
-        if ev is not None:
-            ev[len(calls)].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    per_kernel = {nm: [] for nm in names}
-    step_ms = []
-    for ev in events:
-        for j, nm in enumerate(names):
-            per_kernel[nm].append(ev[j].elapsed_time(ev[j + 1]))
-        step_ms.append(ev[0].elapsed_time(ev[len(names)]))
-    avg = {nm: sum(x) / len(x) for nm, x in per_kernel.items()}
-    ms_per_step = wall * 1e3 / args.steps
-    ev_ms = sum(step_ms) / len(step_ms)
-
-    fwd_fl, bwd_fl = counted_flops(bh, n, d, causal, window)
-    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-    tflops = (fwd_fl + bwd_fl) / (ms_per_step * 1e-3) / 1e12
-    fwd_tf = fwd_fl / (avg["fwd"] * 1e-3) / 1e12
-    bwd_ms = sum(avg[nm] for nm in names if nm != "fwd")
-    bwd_tf = bwd_fl / (bwd_ms * 1e-3) / 1e12
-
-    kfl = kernel_flops(bh, n, d, causal, window)
-    kby = kernel_bytes(bh, n, d, elt)
-    dom = max((nm for nm in names if nm != "preprocess"), key=lambda nm: avg[nm])
-    achieved = kfl[dom] / (avg[dom] * 1e-3) / 1e12
+    kfl = kernel_flops(w.bh, w.n, w.d, causal, window)
+    dom = max((nm for nm in res["kernels"] if nm != "preprocess"), key=lambda nm: res["kernels"][nm]["avg_ms"])
+    dom_ms = res["kernels"][dom]["avg_ms"]
+    achieved = kfl[dom] / (dom_ms * 1e-3) / 1e12
     roofline = {
         "kernel": dom,
         "bound": "mfma",
@@ -332,52 +467,62 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": (measured_traffic(dom)
-                    if (w.name == "headline_8192_d128" and causal and not window and ft == (0, 0)
-                        and kt == (0, 0) and qt == (0, 0) and not args.fused_bwd) else None),
+        "traffic": measured_traffic(dom) if default_run else None,
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
-        "avg_launch_ms": round(avg[dom], 4),
+        "avg_launch_ms": dom_ms,
         "algorithmic_flops_per_launch": kfl[dom],
     }
-    kernels = {}
-    for nm in names:
-        ent = {"avg_ms": round(avg[nm], 4)}
-        if nm in kfl:
-            ent["tflops"] = round(kfl[nm] / (avg[nm] * 1e-3) / 1e12, 1)
-            ent["frac_mfma_peak"] = round(kfl[nm] / (avg[nm] * 1e-3) / 1e12 / peak, 4)
-        ent["hbm_gbs"] = round(kby[nm] / (avg[nm] * 1e-3) / 1e9, 1)
-        kernels[nm] = ent
+    device = {"name": torch.cuda.get_device_name(0),
+              "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
+              "gfx_clock_under_load": clock}
+    if clock and w.dtype == "bf16":
+        # the same fraction against the peak at the clock the chip actually ran at
+        at_clock = device["compute_units"] * 4096 * clock["mhz_median"] * 1e6 / 1e12
+        device["bf16_peak_at_that_clock_tflops"] = round(at_clock, 1)
+        roofline["frac_at_achieved_clock"] = round(achieved / at_clock, 4)
+
+    extra = {}
+    if default_run and not args.no_extra:
+        for key, name, c in (("headline_non_causal", "headline_8192_d128", False),
+                             ("long_context_causal", "long_32768_d128", True)):
+            ws_ = WORKLOADS[name]
+            print(f"# sub-record {key}: {name} causal={c}", file=sys.stderr, flush=True)
+            mm = measure(fa, torch, ws_, c, 0, tiles, False, args.steps, args.warmup)
+            sub = summarize(ws_, c, 0, mm, peak)
+            del mm
+            torch.cuda.empty_cache()
+            sub = {"config": {"workload": name, "batch_heads": ws_.bh, "seq_len": ws_.n, "head_dim": ws_.d,
+                              "causal": c}, **sub}
+            extra[key] = sub
 
     base = None
     if not args.no_cpu_baseline:
-        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        base = cpu_baseline(bh, n, d, causal, args.cpu_budget, window)
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        base = cpu_baseline(w, causal, window, scope=args.cpu_scope if default_run else "sample",
+                            budget_s=args.cpu_budget)
 
     out = {
-        "metric": METRIC,
-        "value": round(tflops, 2),
+        "metric": metric_name(w.dtype, causal, window, w.n, w.d),
+        "value": res["tflops"],
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic: seeded N(0,1) Q, K, V, dO (numpy default_rng(0), cast to bf16)",
-        "config": {"workload": w.name, "batch_heads": bh, "seq_len": n, "head_dim": d,
+        "data": f"synthetic: seeded N(0,1) Q, K, V, dO (numpy default_rng(0), cast to {w.dtype})",
+        "config": {"workload": w.name, "batch_heads": w.bh, "seq_len": w.n, "head_dim": w.d,
                    "causal": causal, "window": window,
-                   "backward": "fused (fa_bwd_fused)" if args.fused_bwd else "two-kernel", "tiles": {"fwd": list(ft), "dkdv": list(kt), "dq": list(qt)}},
-        "pct_of_mfma_peak": round(100 * tflops / peak, 2),
-        "fwd_tflops": round(fwd_tf, 1),
-        "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
-        "bwd_tflops": round(bwd_tf, 1),
-        "bwd_pct_of_peak": round(100 * bwd_tf / peak, 2),
-        "event_ms_per_step": round(ev_ms, 4),
-        "kernels": kernels,
+                   "backward": "fused (fa_bwd_fused)" if args.fused_bwd else "two-kernel",
+                   "tiles": {"fwd": list(tiles[0]), "dkdv": list(tiles[1]), "dq": list(tiles[2])}},
+        **{k: v for k, v in res.items() if k not in ("ms_per_step", "tflops")},
+        "device": device,
         "roofline": roofline,
         "cpu_baseline": base,
+        **extra,
     }
     print(json.dumps(out))
 

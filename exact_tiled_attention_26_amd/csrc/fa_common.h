@@ -183,11 +183,18 @@ struct TrReader {
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-// lds_byte: the wave's LDS destination (byte address, uniform).
+// lds_byte: the wave's LDS destination (byte address, uniform).  M0 is
+// declared clobbered so that the compiler orders this copy against its own
+// M0 writes (the builtin copies and other M0 readers) and never assumes M0
+// survives it; clang warns that M0 is a reserved register, which is the
+// point here, so that warning is silenced for this one statement.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void* gbase, unsigned byte_off, unsigned lds_byte) {
   __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                   :: "v"(byte_off), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_byte)) : "memory");
+                   :: "v"(byte_off), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_byte)) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Asynchronous copy of a ROWS x D bf16 tile (global, row stride D) into a
 // swizzled LDS tile with global_load_lds_dwordx4: lane i of a wave writes the

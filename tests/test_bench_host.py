@@ -74,3 +74,12 @@ def test_traffic_only_for_matching_sources(monkeypatch):
     # ... and not once they have changed since the counter run
     monkeypatch.setattr(bench, "source_hash", lambda kernel: "000000000000")
     assert bench.measured_traffic("dkdv") is None
+
+
+def test_metric_and_data_follow_the_workload():
+    assert bench.metric_name("bf16", True, 0, 8192, 128) == \
+        "fwd+bwd attention TFLOPS (bf16, causal, N=8192, d=128) + % of MFMA peak"
+    assert bench.metric_name("bf16", False, 0, 2048, 64) == \
+        "fwd+bwd attention TFLOPS (bf16, non-causal, N=2048, d=64) + % of MFMA peak"
+    assert bench.metric_name("fp32", True, 256, 4096, 64) == \
+        "fwd+bwd attention TFLOPS (fp32, causal, window 256, N=4096, d=64) + % of MFMA peak"
