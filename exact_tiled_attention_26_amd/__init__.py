@@ -11,7 +11,9 @@ from ._lib import (  # noqa: F401
     FA_ERR_HIP,
     FA_ERR_INVALID_ARG,
     FA_ERR_MISALIGNED,
+    FA_ERR_TOO_LARGE,
     FA_ERR_UNSUPPORTED,
+    FA_NOALLOC_SCRATCH_BYTES,
     FA_OK,
     KERNEL_DKDV,
     KERNEL_DQ,
@@ -24,6 +26,7 @@ from ._lib import (  # noqa: F401
     backward_fused,
     fa_abi_version,
     fa_bwd_fused,
+    fa_bwd_fused_noalloc,
     fa_bwd_fused_workspace_bytes,
     fa_bwd_dkdv,
     fa_bwd_dq,

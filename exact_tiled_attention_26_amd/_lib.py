@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_F32, FA_BF16 = 0, 1
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_HIP = range(5)
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_HIP, FA_ERR_TOO_LARGE = range(6)
+FA_NOALLOC_SCRATCH_BYTES = 1 << 27   # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
 KERNEL_FWD, KERNEL_DKDV, KERNEL_DQ, KERNEL_FUSED = 0, 1, 2, 3
 
 # (name, argtypes) for every function include/fa.h declares
@@ -32,6 +33,7 @@ SIGNATURES = {
     "fa_bwd_dq_rect": [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
     "fa_bwd_fused": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
     "fa_bwd_fused_workspace_bytes": [_I, _I, _I, _I],
+    "fa_bwd_fused_noalloc": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P],
     "fa_default_tiles": [_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "fa_status_str": [_I],
     "fa_abi_version": [],
@@ -45,7 +47,7 @@ class FAError(RuntimeError):
 
 
 _lib = None
-ABI_VERSION = 4   # FA_ABI_VERSION of include/fa.h that SIGNATURES describe
+ABI_VERSION = 5   # FA_ABI_VERSION of include/fa.h that SIGNATURES describe
 
 
 def load_library(path: str = LIB_PATH):
@@ -266,6 +268,23 @@ def fa_bwd_fused(q, k, v, dO, lse, delta, dq, dk, dv, workspace, causal: bool, s
                                      _ptr(dk), _ptr(dv), _ptr(workspace), bh, nq, nk, d, _dtype_code(q), scale,
                                      int(bool(causal)), int(window), int(block_m), int(block_n), _stream(stream))
     _check("fa_bwd_fused", st)
+
+
+def fa_bwd_fused_noalloc(q, k, v, dO, lse, delta, dq, dk, dv, causal: bool, scale: float | None = None,
+                         block_m: int = 0, block_n: int = 0, stream=None, window: int = 0):
+    """fa_bwd_fused without a workspace: bf16 accumulates dQ in the library's
+    fixed device scratch (FA_NOALLOC_SCRATCH_BYTES per GPU); calls that
+    overlap on one GPU race on it."""
+    bh, nq, d = _shape3(q)
+    nk = _kv_shape(q, k)
+    _check_io(q, [("q", q, "io"), ("k", k, "kv"), ("v", v, "kv"), ("dO", dO, "io"), ("lse", lse, "row"),
+                  ("delta", delta, "row"), ("dq", dq, "io"), ("dk", dk, "kv"), ("dv", dv, "kv")], None, kref=k)
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_fused_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dq),
+                                             _ptr(dk), _ptr(dv), bh, nq, nk, d, _dtype_code(q), scale,
+                                             int(bool(causal)), int(window), int(block_m), int(block_n),
+                                             _stream(stream))
+    _check("fa_bwd_fused_noalloc", st)
 
 
 # ------------------------------------------------------------------ allocating helpers

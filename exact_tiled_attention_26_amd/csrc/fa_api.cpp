@@ -133,6 +133,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dim, tiling or size";
     case FA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_TOO_LARGE: return "problem exceeds the fixed scratch of the allocation-free call";
   }
   return "unknown status";
 }
@@ -285,6 +286,33 @@ fa_status fa_bwd_fused(const void* q, const void* k, const void* v, const void* 
                                               st));
   }
   if (any_equal({dq, dk, dv}, {q, k, v, dO, lse, delta, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  return from_hip(fa::launch_bwd_fused_f32((const float*)q, (const float*)k, (const float*)v,
+                                           (const float*)dO, lse, delta, (float*)dq, (float*)dk,
+                                           (float*)dv, bh, nq, nk, d, scale, causal != 0, window,
+                                           block_m, block_n, st));
+}
+
+fa_status fa_bwd_fused_noalloc(const void* q, const void* k, const void* v, const void* dO,
+                               const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                               int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
+                               int causal, int window, int block_m, int block_n, void* stream) {
+  static_assert(FA_NOALLOC_SCRATCH_BYTES == fa::kNoAllocScratchBytes, "one scratch size");
+  fa_status s = check_common(bh, nq, nk, d, dtype);
+  if (s != FA_OK) return s;
+  if ((s = check_scale(scale)) != FA_OK) return s;
+  if (block_m < 0 || block_n < 0) return FA_ERR_INVALID_ARG;
+  if ((s = resolve_tiles(dtype, kFused, d, block_m, block_n)) != FA_OK) return s;
+  bool empty = false;
+  if ((s = check_lengths(bh, nq, nk, causal, window, empty)) != FA_OK || empty) return s;
+  if ((s = check_grid(bh, nk, block_n)) != FA_OK) return s;
+  if ((s = check_ptrs(q, k, v, dO, lse, delta, dq, dk, dv)) != FA_OK) return s;
+  if (any_equal({dq, dk, dv}, {q, k, v, dO, lse, delta, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == FA_BF16) {
+    if ((size_t)bh * (size_t)nq * (size_t)d * sizeof(float) > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+    return from_hip(fa::launch_bwd_fused_bf16_noalloc(q, k, v, dO, lse, delta, dq, dk, dv, bh, nq, nk, d, scale,
+                                                      causal != 0, window, block_m, block_n, st));
+  }
   return from_hip(fa::launch_bwd_fused_f32((const float*)q, (const float*)k, (const float*)v,
                                            (const float*)dO, lse, delta, (float*)dq, (float*)dk,
                                            (float*)dv, bh, nq, nk, d, scale, causal != 0, window,

@@ -34,6 +34,8 @@
 //   (one pass, dQ gathered with fp32 atomic adds) that section 1.4 sets
 //   aside; it is kept for comparison and measured slower on this device.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -728,6 +730,67 @@ hipError_t launch_bwd_fused_bf16(const void* q, const void* k, const void* v, co
   hipLaunchKernelGGL(dq_from_acc_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dq_acc, (__bf16*)dq,
                      n / 4, -scale);   // the fused dK/dV kernel accumulates -dQ / scale
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free single-kernel backward.  Its fp32 dQ accumulator lives in
+// `scratch`, a fixed device array of this library (one copy on every GPU the
+// library runs on, kept until the process ends), so the call needs no
+// workspace argument and never allocates.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address is looked up
+// once per device with hipGetSymbolAddress and only that address is passed
+// to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchFloats = kNoAllocScratchBytes / sizeof(float);
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device that runs `st` (looked up on the
+// first call for that device, with the device current, then cached).
+hipError_t scratch_for_stream(hipStream_t st, float** out) {
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = 0;
+      if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess) return e;
+      if (addr == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<float*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_bwd_fused_bf16_noalloc(const void* q, const void* k, const void* v, const void* dO,
+                                         const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                                         int bh, int nq, int nk, int d, float scale, int causal, int window,
+                                         int bm, int bn, hipStream_t st) {
+  if ((size_t)bh * nq * d > kScratchFloats) return hipErrorInvalidValue;   // the caller checks first
+  float* acc = nullptr;
+  const hipError_t e = scratch_for_stream(st, &acc);
+  if (e != hipSuccess) return e;
+  return launch_bwd_fused_bf16(q, k, v, dO, lse, delta, dq, dk, dv, acc, bh, nq, nk, d, scale, causal, window,
+                               bm, bn, st);
 }
 
 template <int D, int QW, int NW, int BC>

@@ -50,6 +50,14 @@ hipError_t launch_bwd_fused_f32(const float* q, const float* k, const float* v, 
                                 const float* lse, const float* delta, float* dq, float* dk, float* dv,
                                 int bh, int nq, int nk, int d, float scale, int causal, int window,
                                 int bm, int bn, hipStream_t st);
+// The same for bf16 with the fp32 dQ accumulator in the library's fixed
+// device scratch array instead of a caller workspace (no allocation); the
+// caller guarantees bh * nq * d * 4 <= kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 27;
+hipError_t launch_bwd_fused_bf16_noalloc(const void* q, const void* k, const void* v, const void* dO,
+                                         const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                                         int bh, int nq, int nk, int d, float scale, int causal, int window,
+                                         int bm, int bn, hipStream_t st);
 // p[0 .. n) = 0 (a fill kernel, safe under graph capture)
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
 

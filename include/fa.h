@@ -21,6 +21,9 @@
  *   fa_bwd_fused       the single-kernel backward that the two-kernel form
  *                      is weighed against: dK, dV and dQ from one pass over
  *                      the key/value tiles, dQ gathered with atomic adds.
+ *   fa_bwd_fused_noalloc
+ *                      the same without a workspace argument, for callers
+ *                      that cannot allocate device memory.
  *
  * Source of the method (cited by page and section):
  *   "Assignment2: FlashAttention & Distributed Data Parallel notes"
@@ -58,9 +61,11 @@
  *   tilings (0, 0 or the values fa_default_tiles reports).  The result does
  *   not depend on the tiling beyond float rounding.
  * Ownership.  The caller allocates and owns every buffer.  The library never
- *   allocates, frees or synchronises, keeps no state between calls and is
- *   safe to call from several host threads.  Outputs are fully overwritten
- *   (never accumulated into) and must not alias any input.
+ *   allocates, frees or synchronises and is safe to call from several host
+ *   threads.  The only state it keeps is the fixed device scratch array of
+ *   fa_bwd_fused_noalloc (part of the library's device code, one copy per
+ *   GPU) and the cached address of that array on each device.  Outputs are
+ *   fully overwritten (never accumulated into) and must not alias any input.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every call
  *   only enqueues work on it and returns.  The caller orders
  *   fa_bwd_preprocess before fa_bwd_dkdv and fa_bwd_dq (which are
@@ -91,7 +96,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
@@ -100,8 +105,13 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad dtype/scale, aliasing */
   FA_ERR_UNSUPPORTED = 2,   /* head dim, tiling or size not provided */
   FA_ERR_MISALIGNED = 3,    /* a pointer is not 16-byte aligned */
-  FA_ERR_HIP = 4            /* the HIP runtime rejected a launch */
+  FA_ERR_HIP = 4,           /* the HIP runtime rejected a launch */
+  FA_ERR_TOO_LARGE = 5      /* the problem exceeds a fixed capacity (fa_bwd_fused_noalloc) */
 } fa_status;
+
+/* Bytes of the fixed device scratch array behind fa_bwd_fused_noalloc (one
+ * copy on each GPU the library runs on). */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)1 << 27)
 
 /* Forward (CS336 notes 1.2-1.3).  Reads q, k, v; writes o [bh][n][d] and
  * lse [bh][n] (float32, natural log). */
@@ -176,6 +186,26 @@ fa_status fa_bwd_fused(const void* q, const void* k, const void* v, const void* 
 /* Bytes of `workspace` fa_bwd_fused needs: bh * nq * d * 4 for FA_BF16, 0 for
  * FA_F32 (and 0 for non-positive sizes).  Pure host function. */
 size_t fa_bwd_fused_workspace_bytes(int bh, int nq, int d, fa_dtype dtype);
+
+/* Allocation-free single-kernel backward, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of fa_bwd_fused without `workspace`.  FA_BF16 accumulates dQ in float32 in
+ * a fixed device array of the library (FA_NOALLOC_SCRATCH_BYTES bytes, one
+ * copy on each GPU the library runs on, held until the process ends) instead
+ * of a caller workspace; FA_F32 accumulates in dq as fa_bwd_fused does.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); its first call on a device looks up that device's copy of the
+ * array (the device of `stream`).  With FA_BF16, bh * nq * d * 4 >
+ * FA_NOALLOC_SCRATCH_BYTES returns FA_ERR_TOO_LARGE before any HIP call.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call clears it before use): calls that overlap on one GPU
+ * (on concurrent streams or from several host threads) race on it and must
+ * be serialised by the caller. */
+fa_status fa_bwd_fused_noalloc(const void* q, const void* k, const void* v, const void* dO,
+                               const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                               int bh, int nq, int nk, int d, fa_dtype dtype, float scale,
+                               int causal, int window, int block_m, int block_n, void* stream);
 
 /* The tiling (block_m, block_n) that block_m = block_n = 0 selects for a
  * kernel (0 = fwd, 1 = dkdv, 2 = dq, 3 = fused backward) at this dtype and

@@ -46,8 +46,8 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strings(lib):
-    assert fa.fa_abi_version() == 4
-    for code in range(5):
+    assert fa.fa_abi_version() == 5
+    for code in range(6):
         assert fa.fa_status_str(code)
     assert fa.fa_status_str(99) == "unknown status"
 
@@ -291,3 +291,30 @@ def test_c_client_links_and_reports_abi(lib):
     # bad arguments are refused before any HIP call
     r = subprocess.run([C_CLIENT, "in", "out", "0", "8", "64", "1"], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1
+
+
+def noalloc(lib, **kw):
+    a = dict(q=A, k=B, v=C, dO=D_, lse=E, delta=F, dq=G, dk=H, dv=0x90000, bh=1, nq=64, nk=64, d=64,
+             dtype=fa.FA_BF16, scale=0.125, causal=1, window=0, bm=0, bn=0)
+    a.update(kw)
+    return lib.fa_bwd_fused_noalloc(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"], a["dq"], a["dk"],
+                                    a["dv"], a["bh"], a["nq"], a["nk"], a["d"], a["dtype"], a["scale"],
+                                    a["causal"], a["window"], a["bm"], a["bn"], None)
+
+
+def test_noalloc_rejects_what_exceeds_its_scratch(lib):
+    """The allocation-free backward's fixed scratch holds bh * nq * d float32
+    values up to FA_NOALLOC_SCRATCH_BYTES; a larger bf16 call is refused on
+    the host, before any HIP call (the fake pointers are never touched)."""
+    cap = fa.FA_NOALLOC_SCRATCH_BYTES // 4
+    assert noalloc(lib, bh=cap // (8192 * 128) + 1, nq=8192, nk=8192, d=128) == fa.FA_ERR_TOO_LARGE
+    assert noalloc(lib, bh=1, nq=cap // 64 + 1, nk=cap // 64 + 1, d=64) == fa.FA_ERR_TOO_LARGE
+    assert "scratch" in fa.fa_status_str(fa.FA_ERR_TOO_LARGE)
+    # the usual argument checks come first and are those of fa_bwd_fused
+    assert noalloc(lib, dq=0) == fa.FA_ERR_INVALID_ARG
+    assert noalloc(lib, dq=A) == fa.FA_ERR_INVALID_ARG
+    assert noalloc(lib, dk=0x90008) == fa.FA_ERR_MISALIGNED
+    assert noalloc(lib, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert noalloc(lib, bm=64, bn=64) == fa.FA_ERR_UNSUPPORTED
+    assert noalloc(lib, window=8, causal=0) == fa.FA_ERR_INVALID_ARG
+    assert noalloc(lib, bh=0) == fa.FA_OK
