@@ -238,9 +238,10 @@ def _stats(xs):
 
 def measure(fa, torch, w, causal, window, tiles, fused, steps, warmup):
     """Time `steps` whole steps (forward, preprocess, dK/dV, dQ, or the fused
-    backward) on the workload's seeded inputs, after `warmup` untimed ones.
-    Returns the wall time per step and per-kernel HIP-event times; every
-    event is recorded on the stream the kernels are launched on."""
+    backward) on the workload's seeded inputs, after `warmup` untimed ones:
+    the wall time per step over one pass with nothing between the calls, and
+    per-kernel HIP-event times over a second pass (every event recorded on
+    the stream the kernels are launched on)."""
     from workloads import cast_io, make_inputs
 
     bh, n, d = w.bh, w.n, w.d
@@ -285,13 +286,19 @@ def measure(fa, torch, w, causal, window, tiles, fused, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the wall clock over `steps` whole steps, with nothing between the calls
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel HIP events in a second pass (the event records add a little
+    # time of their own between the kernels)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_kernel = {nm: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, nm in enumerate(names)}
     return {"names": names, "ms_per_step": wall * 1e3 / steps,
             "event_ms_per_step": sum(ev[0].elapsed_time(ev[len(names)]) for ev in events) / steps,
@@ -332,11 +339,12 @@ def summarize(w, causal, window, m, peak):
     }
 
 
-def sample_clock(step, seconds=1.0):
+def sample_clock(step, seconds=3.0, settle=1.5):
     """Shader (GFX) clock while the timed step runs back to back for about
     `seconds`: the mean over the GPU's XCDs of amdsmi's current_gfxclks,
-    sampled every 10 ms; the first 30 % of the run (clock ramp) is dropped.
-    Returns None where amdsmi is not available."""
+    sampled every 10 ms, keeping the samples taken after `settle` seconds
+    (the metrics table trails the load by up to about a second).  Returns
+    None where amdsmi is not available."""
     import threading
 
     import torch
@@ -369,7 +377,7 @@ def sample_clock(step, seconds=1.0):
     stop.set()
     th.join()
     t1 = time.perf_counter()
-    kept = [c for t, c in samples if t >= t0 + 0.3 * (t1 - t0)]
+    kept = [c for t, c in samples if t >= t0 + settle]
     try:
         amdsmi.amdsmi_shut_down()
     except Exception:
@@ -378,8 +386,9 @@ def sample_clock(step, seconds=1.0):
         return None
     kept.sort()
     return {"mhz_median": round(kept[len(kept) // 2], 1), "mhz_min": round(kept[0], 1), "mhz_max": round(kept[-1], 1),
-            "samples": len(kept), "source": "amdsmi current_gfxclks (mean over XCDs), sampled every 10 ms while "
-                                            "the timed step ran back to back for about 1 s"}
+            "samples": len(kept), "source": f"amdsmi current_gfxclks (mean over XCDs), sampled every 10 ms while "
+                                            f"the timed step ran back to back for {seconds:.0f} s, after the first "
+                                            f"{settle:.1f} s"}
 
 
 def main():

@@ -130,10 +130,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running max (exponent base) and this lane's part of the running sum
-  float m[NQB], lsum[NQB];
+  // running max (exponent base) and this lane's part of the running sum;
+  // mb = m, or 0 while m = -inf (so that -inf - (-inf) never occurs), and
+  // mraw = (m + slack) / (scale log2 e), the vote's threshold in raw score
+  // units; both change only where m does
+  float m[NQB], lsum[NQB], mb[NQB], mraw[NQB];
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) { m[qb] = kNegInf; lsum[qb] = 0.f; }
+  for (int qb = 0; qb < NQB; ++qb) { m[qb] = kNegInf; lsum[qb] = 0.f; mb[qb] = 0.f; mraw[qb] = kNegInf; }
+  const float inv_sl2 = 1.f / scale_log2;
 
   const NatReader<D> kread(l16, g);
   const TrReader<D> vread(l16, g);
@@ -159,7 +163,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int i = 0; i < 4; ++i)
       if (16 * kb + i > lim || (BAND && 16 * kb + i <= llim)) s[kb][qb][i] = kNegInf;
   };
-  // scaled max (base 2) of one query block over this lane's 16 keys of the
+  // raw (unscaled) max of one query block over this lane's 16 keys of the
   // tile; the other three lanes of the query hold the rest of the row
   auto row_max = [&](f32x4 (&s)[NKB][NQB], int qb) __attribute__((always_inline)) {
     float t = kNegInf;
@@ -167,22 +171,27 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) t = fmaxf(t, s[kb][qb][i]);
-    return t * scale_log2;
+    return t;
   };
   // raise the exponent base when some score outgrew it by the slack.  The
-  // test needs only each lane's partial max and a vote (read into a scalar
-  // register, so the branch is uniform); the full row max is formed in the
-  // rare taken branch.
+  // test needs only each lane's partial max and a vote (a wave ballot, which
+  // lands in scalar registers, so the branch is uniform); the full row max
+  // is formed in the rare taken branch.
+  // (the test compares raw maxima with mraw, which is equivalent because the
+  // scale is positive; a rounding at the boundary only lets a probability
+  // reach 2^8 by one ulp more)
   auto update_base = [&](const float (&mx)[NQB]) __attribute__((always_inline)) {
     bool grow = false;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) grow |= !(mx[qb] <= m[qb] + kRescaleSlack);   // true while m = -inf
-    if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
+    for (int qb = 0; qb < NQB; ++qb) grow |= !(mx[qb] <= mraw[qb]);   // true while m = -inf
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        const float m_new = fmaxf(m[qb], wave_max_rows(mx[qb]));
+        const float m_new = fmaxf(m[qb], wave_max_rows(mx[qb]) * scale_log2);
         const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(m[qb] - m_new);
         m[qb] = m_new;
+        mb[qb] = (m_new == kNegInf) ? 0.f : m_new;
+        mraw[qb] = (m_new + kRescaleSlack) * inv_sl2;
         lsum[qb] *= corr;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[db][qb] *= corr;
@@ -246,15 +255,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                   int t, auto has_next, auto next_masked) __attribute__((always_inline)) {
     constexpr bool HN = decltype(has_next)::value;
     constexpr bool NM = decltype(next_masked)::value;
-    float m_use[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) m_use[qb] = (m[qb] == kNegInf) ? 0.f : m[qb];   // never (-inf) - (-inf)
     bf16x8 pb[NKS][NQB];
     // probability item e: score (kb, qb, i) in the order of the PV halves
     auto p_item = [&](int e) __attribute__((always_inline)) {
       const int h = e / (NE / 2), r = e % (NE / 2);
       const int qb = r / 8, kb = 2 * h + (r / 4) % 2, i = r % 4;
-      const float p = exp2_fast(__builtin_fmaf(sc[kb][qb][i], scale_log2, -m_use[qb]));
+      const float p = exp2_fast(__builtin_fmaf(sc[kb][qb][i], scale_log2, -mb[qb]));
       sc[kb][qb][i] = p;
       lsum[qb] += p;   // fp32: the row sum sets L, which bf16 terms would not resolve
       if (r % 8 == 7) pb[h][qb] = pack_bf16(sc[2 * h][qb], sc[2 * h + 1][qb]);
