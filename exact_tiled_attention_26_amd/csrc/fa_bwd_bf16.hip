@@ -112,7 +112,9 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int it0 = CAUSAL ? max(0, k0 - off) / BR : 0;   // earlier query rows see none of these keys
   // later rows see none of them either once the window has moved past them
   const int it1 = BAND ? min(ntq, max(0, k0 + BC - 2 - lo) / BR + 1) : ntq;
-  // compiler-visible copies: measured faster than the hidden form here
+  // compiler-visible copies: with them the compiler waits for all LDS reads
+  // (lgkmcnt(0)) at each operand use, yet the hidden form (exact wait counts,
+  // with the row loads below hidden as well) measured 4 % slower here
   const AsyncTileCopy<D, BR, NW, false> copier(wave, lane);
   auto issue_tile = [&](__bf16* qd, __bf16* od, float* ld, float* dd, int i0) __attribute__((always_inline)) {
     copier.issue(qd, Qh + (size_t)i0 * D, nq - i0);
@@ -512,8 +514,9 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int kend = CAUSAL ? min(nk, q0 + BR + off) : nk;
   const int jt0 = BAND ? max(0, q0 + lo + 1) / BC : 0;   // first key tile a row of the workgroup can see
   const int ntk = (kend + BC - 1) / BC;
-  // compiler-visible copies: measured faster than the hidden form here
-  const AsyncTileCopy<D, BC, NW, false> copier(wave, lane);
+  // hidden copies: the compiler keeps exact LDS wait counts for the operand
+  // reads (measured 1-2 % faster than the compiler-visible form)
+  const AsyncTileCopy<D, BC, NW, true> copier(wave, lane);
   copier.issue(k_lds0, Kh + (size_t)jt0 * BC * D, nk - jt0 * BC);
   copier.issue(v_lds0, Vh + (size_t)jt0 * BC * D, nk - jt0 * BC);
 
