@@ -221,15 +221,21 @@ struct AsyncTileCopy {
       const int r = p / NCH;
       const int c = (p % NCH) ^ swz_sigma<D>(r);
       src_off[i] = r * D + c * 8;
-      lds_off[i] = slot0 * 8;
+      // uniform per wave: read into a scalar register once, so that no copy
+      // needs a lane read to form its M0 value
+      lds_off[i] = __builtin_amdgcn_readfirstlane(slot0 * 8);
     }
   }
   // Copy rows [0, ROWS) of the tile starting at g; `valid` >= 1 rows exist.
+  // (the empty volatile statement in the partial-tile branch keeps the
+  // compiler from merging the two branches into per-lane selects, which
+  // would put the partial-tile arithmetic in front of every full-tile copy)
   __device__ __forceinline__ void issue(__bf16* tile, const __bf16* g, int valid) const {
     if (valid >= ROWS) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) issue_one(tile + lds_off[i], g, src_off[i]);
     } else {
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int row = src_off[i] / D;   // D is a power of two
@@ -245,6 +251,7 @@ struct AsyncTileCopy {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) issue_one_at(tile_byte + 2u * lds_off[i], g, src_off[i]);
     } else {
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int row = src_off[i] / D;
@@ -257,7 +264,7 @@ struct AsyncTileCopy {
     if constexpr (HIDDEN) {
       lds_dma16(g, 2u * off, lds_byte);
     } else {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const char*)g + 2u * (unsigned)off),
                                        (__attribute__((address_space(3))) void*)(uintptr_t)lds_byte, 16, 0, 0);
     }
   }
@@ -265,7 +272,7 @@ struct AsyncTileCopy {
     if constexpr (HIDDEN) {
       lds_dma16(g, 2u * off, lds_address(lds));
     } else {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const char*)g + 2u * (unsigned)off),
                                        (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
     }
   }
