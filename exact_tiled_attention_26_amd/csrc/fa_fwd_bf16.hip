@@ -297,6 +297,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
 #pragma unroll
         for (int e = u * EA / US; e < (u + 1) * EA / US; ++e) p_item(e);
+        // order within the step: product, vector op, LDS read, product,
+        // vector op, the rest after (measured about 1 % faster causal than
+        // the compiler's own order; the same in phase B measured no gain)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
