@@ -1,12 +1,15 @@
-"""The torch autograd drop-in (``flash_attention``) against torch CPU autograd
-of the plain definition, in float64, on seeded random inputs.
+"""The torch autograd drop-in (``flash_attention``) against the fp64 oracle and,
+as a second referee, torch CPU autograd of the plain definition, in float64,
+on seeded random inputs.
 
-The reference is softmax(scale * Q K^T) V with keys after the query masked
-(causal), differentiated by torch on the CPU; the inputs are the exact values
-of the device tensors (bf16 values upcast), so input rounding is not charged
-to the kernels.  Tolerances are the parity tests': float32 I/O: outputs 1e-5
-absolute, gradients 1e-4 of the largest reference gradient; bf16 I/O: outputs
-1e-2, gradients 3e-2.
+The loss is sum(O * W), so dO = W: the oracle's forward and backward
+(``oracle.attention_forward`` / ``attention_backward``) give the expected O
+and gradients directly; torch's reference is softmax(scale * Q K^T) V with
+the end-aligned causal mask (and window), differentiated by torch on the CPU.
+The inputs are the exact values of the device tensors (bf16 values upcast),
+so input rounding is not charged to the kernels.  Tolerances are the parity
+tests': float32 I/O: outputs 1e-5 absolute, gradients 1e-4 of the largest
+reference gradient; bf16 I/O: outputs 1e-2, gradients 3e-2.
 """
 
 import math
@@ -16,6 +19,7 @@ import pytest
 import torch
 
 import exact_tiled_attention_26_amd as fa
+import oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +48,20 @@ def _rel(err, ref):
     return err / (m if m > 0 else 1.0)
 
 
+def _check_against_oracle(out, grads, q, k, v, w, causal, window, tol_o, tol_g):
+    """O and (dQ, dK, dV) of the device call against the oracle on the same
+    values, with dO = W (the gradient of sum(O * W))."""
+    q, k, v, w = (t.detach().cpu().double().reshape(-1, *t.shape[-2:]).numpy() for t in (q, k, v, w))
+    o_ref, _ = oracle.attention_forward(q, k, v, causal=causal, window=window)
+    dq_ref, dk_ref, dv_ref, _ = oracle.attention_backward(q, k, v, w, causal=causal, window=window)
+    err_o = abs(out.detach().cpu().double().reshape(o_ref.shape).numpy() - o_ref).max()
+    assert err_o <= tol_o, ("oracle", "o", err_o)
+    for name, a, b in (("dq", grads[0], dq_ref), ("dk", grads[1], dk_ref), ("dv", grads[2], dv_ref)):
+        b = torch.from_numpy(b)
+        err = _rel((a.cpu().double().reshape(b.shape) - b).abs().max().item(), b)
+        assert err <= tol_g, ("oracle", name, err)
+
+
 @pytest.mark.parametrize("dtype,shape,nk", [(torch.float32, (2, 3, 77, 32), 77),
                                             (torch.bfloat16, (2, 2, 300, 64), 300),
                                             (torch.float32, (2, 2, 50, 32), 130),
@@ -66,6 +84,7 @@ def test_matches_cpu_autograd(dtype, shape, nk, causal):
     (ref * wd.cpu().double()).sum().backward()
 
     tol_o, tol_g = TOL[dtype]
+    _check_against_oracle(out, (qd.grad, kd.grad, vd.grad), qd, kd, vd, wd, causal, 0, tol_o, tol_g)
     assert out.shape == ref.shape == q.shape and out.dtype == dtype
     err_o = (out.detach().cpu().double() - ref.detach()).abs().max().item()
     assert err_o <= tol_o, err_o
@@ -94,6 +113,7 @@ def test_window_matches_cpu_autograd(dtype, shape, nk, window):
     (ref * wd.cpu().double()).sum().backward()
 
     tol_o, tol_g = TOL[dtype]
+    _check_against_oracle(out, (qd.grad, kd.grad, vd.grad), qd, kd, vd, wd, True, window, tol_o, tol_g)
     err_o = (out.detach().cpu().double() - ref.detach()).abs().max().item()
     assert err_o <= tol_o, err_o
     for name, a, b in (("dq", qd.grad, qc.grad), ("dk", kd.grad, kc.grad), ("dv", vd.grad, vc.grad)):
