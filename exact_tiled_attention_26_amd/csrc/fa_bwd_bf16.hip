@@ -73,7 +73,7 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                       const float* __restrict__ LSE, const float* __restrict__ DELTA,
                       __bf16* __restrict__ dK, __bf16* __restrict__ dV, float* __restrict__ dQacc,
-                      int bh, int nq, int nk, int window, float scale, float scale_log2) {
+                      int bh, int nq, int nk, int window, int hg, float scale, float scale_log2) {
   constexpr int BC = KW * NW;
   constexpr int NKB = KW / 16;   // 16-key blocks per wave
   constexpr int NDS = D / 32;
@@ -95,8 +95,9 @@ void dkdv_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int head = blockIdx.x % bh;
-  const int kt = blockIdx.x / bh;          // causal: tile 0 sees the most queries
+  const int nkt = (nk + KW * NW - 1) / (KW * NW);
+  int head, kt;   // causal: key tile 0 sees the most queries, so it goes first
+  head_and_tile(blockIdx.x, bh, nkt, hg, head, kt);
   const int k0 = kt * BC;
   const int k0w = k0 + wave * KW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, (BC == 32 || D == 64) ? 2 : 1)
 void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                     const float* __restrict__ LSE, const float* __restrict__ DELTA,
-                    __bf16* __restrict__ dQ, int bh, int nq, int nk, int window, float scale,
+                    __bf16* __restrict__ dQ, int bh, int nq, int nk, int window, int hg, float scale,
                     float scale_log2) {
   constexpr int BR = QW * NW;
   constexpr int NQB = QW / 16;
@@ -501,8 +502,9 @@ void dq_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int ntq = (nq + BR - 1) / BR;
-  const int head = blockIdx.x % bh;
-  const int qt = ntq - 1 - blockIdx.x / bh;
+  int head, rank;
+  head_and_tile(blockIdx.x, bh, ntq, hg, head, rank);
+  const int qt = ntq - 1 - rank;   // heaviest (causal: last) query tile first
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
@@ -691,9 +693,10 @@ static hipError_t launch_dkdv_inst(const void* q, const void* k, const void* v, 
   auto kern = (causal && window > 0) ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, true, FUSED>
              : causal ? dkdv_bf16_kernel<D, KW, NW, BR, true, true, false, FUSED>
                       : dkdv_bf16_kernel<D, KW, NW, BR, false, true, false, FUSED>;
+  const int hg = head_group((const void*)kern, NW * 64, bh, ntk, st);
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                      (const __bf16*)dO, lse, delta, (__bf16*)dk, (__bf16*)dv, dqacc, bh, nq, nk, window,
-                     scale, sl2);
+                     hg, scale, sl2);
   return hipGetLastError();
 }
 
@@ -808,8 +811,9 @@ static hipError_t launch_dq_inst(const void* q, const void* k, const void* v, co
   auto kern = (causal && window > 0) ? dq_bf16_kernel<D, QW, NW, BC, true, true>
              : causal ? dq_bf16_kernel<D, QW, NW, BC, true, false>
                       : dq_bf16_kernel<D, QW, NW, BC, false, false>;
+  const int hg = head_group((const void*)kern, NW * 64, bh, ntq, st);
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (const __bf16*)dO, lse, delta, (__bf16*)dq, bh, nq, nk, window, scale, sl2);
+                     (const __bf16*)dO, lse, delta, (__bf16*)dq, bh, nq, nk, window, hg, scale, sl2);
   return hipGetLastError();
 }
 

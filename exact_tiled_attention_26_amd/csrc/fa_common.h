@@ -80,6 +80,23 @@ __device__ __forceinline__ int divergent_zero() {
   return z;
 }
 
+// Workgroup order over (head, tile).  Workgroups are dispatched in id order
+// and dealt to the 8 XCDs round robin, each XCD with its own L2.  Heads go in
+// groups of hg (a multiple of 8 unless it is all bh heads): id runs over the
+// tiles of one group before the next, tile index = rank within the group,
+// heaviest first, and head = first head of the group + id mod the group's
+// size, so all tiles of a head land on one XCD and a group's tiles are in
+// flight together, sharing the head's K/V (or Q/dO) through that L2.  With
+// hg = bh this is the plain order head = id mod bh, tile = id / bh.
+__device__ __forceinline__ void head_and_tile(int id, int bh, int ntiles, int hg, int& head, int& tile) {
+  const int span = hg * ntiles;
+  const int grp = id / span;
+  const int r = id - grp * span;
+  const int gsz = min(hg, bh - grp * hg);
+  head = grp * hg + r % gsz;
+  tile = r / gsz;
+}
+
 // Lower edge of the visible keys: key j is hidden from query i when
 // j <= i + lo.  Without a window no key is hidden from below.
 __device__ __forceinline__ int window_lo(bool causal, int off, int window) {

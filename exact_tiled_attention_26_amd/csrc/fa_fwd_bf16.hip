@@ -32,8 +32,9 @@
 //   most 2^kRescaleSlack and the final O = acc / l and L = m + log2 l are
 //   unchanged (the same stale m enters numerator, denominator and L).
 // * Workgroup ids are mapped heaviest query tile first (causal work grows
-//   with the tile index), and head = id mod bh keeps every tile of a head on
-//   one XCD (ids are dealt to the 8 XCDs round robin) for L2 reuse of K/V.
+//   with the tile index) within groups of heads whose tiles are all in
+//   flight together, every tile of a head on one XCD, for L2 reuse of K/V
+//   (head_and_tile).
 #include <type_traits>
 
 #include "fa_common.h"
@@ -57,7 +58,7 @@ template <int D, int QW, int NW, int BC, bool CAUSAL, bool RAGGED, bool BAND, in
 __global__ __launch_bounds__(NW * 64, 2)
 void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                     float* __restrict__ LSE, int bh, int nq, int nk, int window,
+                     float* __restrict__ LSE, int bh, int nq, int nk, int window, int hg,
                      float scale_log2) {
   constexpr int BR = QW * NW;
   constexpr int NQB = QW / 16;   // 16-query blocks per wave
@@ -82,8 +83,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int ntq = (nq + BR - 1) / BR;
-  const int head = blockIdx.x % bh;
-  const int qt = ntq - 1 - blockIdx.x / bh;
+  int head, rank;
+  head_and_tile(blockIdx.x, bh, ntq, hg, head, rank);
+  const int qt = ntq - 1 - rank;   // heaviest (causal: last) query tile first
   const int q0 = qt * BR;
   const int q0w = q0 + wave * QW;
   const int off = CAUSAL ? nk - nq : 0;   // query i sees keys 0 .. i + off
@@ -471,8 +473,9 @@ static hipError_t launch_fwd_inst(const void* q, const void* k, const void* v, v
             : causal ? fwd_bf16_kernel<D, QW, NW, BC, true, true, false, NB>
             : (nk % BC) ? fwd_bf16_kernel<D, QW, NW, BC, false, true, false, NB>
                        : fwd_bf16_kernel<D, QW, NW, BC, false, false, false, NB>;
+  const int hg = head_group((const void*)kern, NW * 64, bh, ntq, st);
   hipLaunchKernelGGL(kern, grid, block, 0, st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (__bf16*)o, lse, bh, nq, nk, window, sl2);
+                     (__bf16*)o, lse, bh, nq, nk, window, hg, sl2);
   return hipGetLastError();
 }
 
