@@ -29,7 +29,8 @@
 // * Causal mode visits only the tiles that hold a visible (query, key) pair
 //   and masks only tiles crossing the diagonal; a sliding window (BAND
 //   instances) also bounds the loops from the band's other edge.  Workgroups
-//   are ordered with the heaviest tiles first.
+//   are ordered with the heaviest tiles first (within groups of heads when
+//   there are many heads: head_and_tile).
 // * The FUSED instance of the dK/dV kernel is the single-kernel alternative
 //   (one pass, dQ gathered with fp32 atomic adds) that section 1.4 sets
 //   aside; it is kept for comparison and measured slower on this device.
