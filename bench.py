@@ -65,9 +65,9 @@ def kernel_bytes(bh, n, d, elt):
 
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "attention_kernels_headline_8192_d128_causal_bf16.md")
 KERNEL_SOURCES = {
-    "fwd": ("fa_fwd_bf16.hip", "fa_common.h", "fa_order.cpp"),
-    "dkdv": ("fa_bwd_bf16.hip", "fa_common.h", "fa_order.cpp"),
-    "dq": ("fa_bwd_bf16.hip", "fa_common.h", "fa_order.cpp"),
+    "fwd": ("fa_fwd_bf16.hip", "fa_common.h", "fa_order.h", "fa_order.cpp"),
+    "dkdv": ("fa_bwd_bf16.hip", "fa_common.h", "fa_order.h", "fa_order.cpp"),
+    "dq": ("fa_bwd_bf16.hip", "fa_common.h", "fa_order.h", "fa_order.cpp"),
     "preprocess": ("fa_f32.hip",),
 }
 

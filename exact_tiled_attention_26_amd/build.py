@@ -5,7 +5,8 @@ Python.  Every source under ``csrc/`` is compiled with hipcc for gfx950 into
 ``_build/`` (in parallel) and linked into ``libfa.so`` next to this file.
 ``build_c_client()`` also compiles the plain C client of the ABI that the
 tests run (``tests/c_abi/fa_c_client.c``, host code only, linked against
-libfa.so).
+libfa.so), and ``build_order_check()`` the host-side check of the workgroup
+order (``tests/c_abi/order_check.cpp``).
 """
 
 from __future__ import annotations
@@ -93,7 +94,26 @@ def build_c_client(verbose: bool = False) -> str:
     return C_CLIENT
 
 
+ORDER_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "order_check.cpp")
+ORDER_CHECK = os.path.join(ROOT, "tests", "c_abi", "_build", "order_check")
+
+
+def build_order_check(verbose: bool = False) -> str:
+    """Compile the host-side check of the workgroup order (csrc/fa_order.h)
+    with hipcc as host code only; it runs on the CPU."""
+    os.makedirs(os.path.dirname(ORDER_CHECK), exist_ok=True)
+    cmd = [_hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "--offload-host-only", "-O2", "-std=c++17",
+           "-Wall", ORDER_CHECK_SRC, "-o", ORDER_CHECK]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"order check build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {ORDER_CHECK}")
+    return ORDER_CHECK
+
+
 if __name__ == "__main__":
     build(verbose=True)
     build_c_client(verbose=True)
+    build_order_check(verbose=True)
     sys.exit(0)

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_order.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -78,23 +80,6 @@ __device__ __forceinline__ int divergent_zero() {
   int z;
   __asm__ volatile("v_mov_b32 %0, 0" : "=v"(z));
   return z;
-}
-
-// Workgroup order over (head, tile).  Workgroups are dispatched in id order
-// and dealt to the 8 XCDs round robin, each XCD with its own L2.  Heads go in
-// groups of hg (a multiple of 8 unless it is all bh heads): id runs over the
-// tiles of one group before the next, tile index = rank within the group,
-// heaviest first, and head = first head of the group + id mod the group's
-// size, so all tiles of a head land on one XCD and a group's tiles are in
-// flight together, sharing the head's K/V (or Q/dO) through that L2.  With
-// hg = bh this is the plain order head = id mod bh, tile = id / bh.
-__device__ __forceinline__ void head_and_tile(int id, int bh, int ntiles, int hg, int& head, int& tile) {
-  const int span = hg * ntiles;
-  const int grp = id / span;
-  const int r = id - grp * span;
-  const int gsz = min(hg, bh - grp * hg);
-  head = grp * hg + r % gsz;
-  tile = r / gsz;
 }
 
 // Lower edge of the visible keys: key j is hidden from query i when

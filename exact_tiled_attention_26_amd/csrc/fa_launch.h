@@ -61,12 +61,10 @@ hipError_t launch_bwd_fused_bf16_noalloc(const void* q, const void* k, const voi
 // p[0 .. n) = 0 (a fill kernel, safe under graph capture)
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
 
-// Heads per group for the workgroup order (head_and_tile in fa_common.h):
-// all bh heads (the plain order) when the device holds at least 4 bh
-// workgroups at once, else as many heads as have all their ntiles tiles
-// resident at once, rounded down to a multiple of 8, at least 8 and at most
-// bh.  `kern` and `threads` give the residency (workgroups per CU, from the
-// occupancy query, times the device's CUs), cached per device and kernel.
+// Heads per group for the workgroup order (fa_order.h), from how many
+// workgroups of `kern` (`threads` each) the stream's device runs at once:
+// the occupancy query's workgroups per CU times the device's CUs, cached
+// per device and kernel.
 int head_group(const void* kern, int threads, int bh, int ntiles, hipStream_t st);
 
 // dtype: 0 = float32, 1 = bf16

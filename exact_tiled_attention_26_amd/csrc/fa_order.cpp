@@ -1,9 +1,10 @@
-// Host side of the workgroup order (head_and_tile in fa_common.h): how many
-// heads go in one group, from how many workgroups the device holds at once.
+// Host side of the workgroup order (fa_order.h): how many heads go in one
+// group, from how many workgroups the device holds at once.
 #include <atomic>
 #include <mutex>
 
 #include "fa_launch.h"
+#include "fa_order.h"
 
 namespace fa {
 
@@ -57,23 +58,21 @@ int per_cu(const void* kern, int threads) {
   return n;
 }
 
-}  // namespace
-
-int head_group(const void* kern, int threads, int bh, int ntiles, hipStream_t st) {
+// workgroups of `kern` the stream's device runs at once
+int resident_workgroups(const void* kern, int threads, hipStream_t st) {
   int dev = 0;
   if (hipStreamGetDevice(st, &dev) != hipSuccess) {
     (void)hipGetLastError();
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   }
-  const int resident = cu_count(dev) * per_cu(kern, threads);
-  // with few heads the plain order already has several tiles of each head in
-  // flight (4 or more); grouping them then measured 2-5 % slower on the
-  // causal N 8192 headline, and 10-17 % faster with hundreds of heads
-  if (resident >= 4 * bh) return bh;
-  int hg = resident / (ntiles > 0 ? ntiles : 1);
-  hg -= hg % 8;
-  if (hg < 8) hg = 8;
-  return hg >= bh ? bh : hg;
+  const int n = cu_count(dev) * per_cu(kern, threads);
+  return n > 0 ? n : 1;
+}
+
+}  // namespace
+
+int head_group(const void* kern, int threads, int bh, int ntiles, hipStream_t st) {
+  return head_group_for(bh, ntiles, resident_workgroups(kern, threads, st));
 }
 
 }  // namespace fa
