@@ -72,7 +72,7 @@ def fp32_large_score_tol(g, causal, scale=None):
 
 def compare_full(g, dtype, causal, scale=None, label="", window=0, tol_override=None):
     """Whole-tensor comparison with the oracle; returns the error report.
-    `tol_override` replaces some of the benchmark spec's bounds (only the float32
+    `tol_override` replaces some of the bounds in TOL (only the float32
     large-score test passes one, derived in fp32_large_score_tol)."""
     tol = dict(TOL[dtype])
     tol.update(tol_override or {})
