@@ -53,7 +53,7 @@ def _rel(err, ref):
 
 def fp32_large_score_tol(g, causal, scale=None):
     """O and L bounds for float32 inputs whose scores are far larger than
-    the N(0, 1) workloads' (reading 10).  Every fp32 rounding on the way to
+    the N(0, 1) workloads'.  Every fp32 rounding on the way to
     a probability (the dot-product accumulation, the scale multiply, the
     subtraction of the row max) can move the exponent by up to max|S| 2^-24;
     allowing 8 of them gives a relative error eps = 8 max|S| 2^-24 on each
@@ -250,7 +250,7 @@ def rising_inputs(bh, n, d, step2, seed, v_scale=0.5, tile=64, a=512.0):
 @pytest.mark.parametrize("step2", [7.0, 12.0])
 def test_lazy_rescale_rising_scores(step2, d, causal):
     """The bf16 forward keeps a stale exponent base until a score beats it
-    by more than 2^8 (reading 16) and then rescales the accumulator and the
+    by more than 2^8 and then rescales the accumulator and the
     running sum by exp2(m_old - m_new) < 1 ([CS336-A2] 1.2).  With scores
     rising by 12 per 64-key tile every tile moves the base; with 7 the base
     moves every other tile and stays up to 2^7 stale in between.  Checked
