@@ -112,8 +112,28 @@ def build_order_check(verbose: bool = False) -> str:
     return ORDER_CHECK
 
 
+SWIZZLE_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "swizzle_check.cpp")
+SWIZZLE_CHECK = os.path.join(ROOT, "tests", "c_abi", "_build", "swizzle_check")
+
+
+def build_swizzle_check(verbose: bool = False) -> str:
+    """Compile the host-side check of the bf16 LDS tile layout (the copy
+    placement, the readers' offsets and the bank model in csrc/fa_common.h)
+    with hipcc as host code only; it runs on the CPU."""
+    os.makedirs(os.path.dirname(SWIZZLE_CHECK), exist_ok=True)
+    cmd = [_hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "--offload-host-only", "-O2", "-std=c++17",
+           "-Wall", SWIZZLE_CHECK_SRC, "-o", SWIZZLE_CHECK]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"swizzle check build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SWIZZLE_CHECK}")
+    return SWIZZLE_CHECK
+
+
 if __name__ == "__main__":
     build(verbose=True)
     build_c_client(verbose=True)
     build_order_check(verbose=True)
+    build_swizzle_check(verbose=True)
     sys.exit(0)

@@ -120,17 +120,25 @@ __device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
 //   row R0 + l16 (R0 a multiple of 16);
 // * transposed: lane (g, l16) reads half of chunk 2 db + (l16 / 2) % 2 of row
 //   R0 + 4 g + l16 / 4.
-// sigma below makes both conflict-free (checked exhaustively against that
-// model for every ds, db and R0): for D = 128, sigma(r) = (r mod 16) xor
-// (12 (r mod 2)); for D = 64 (two rows per bank sweep), sigma(r) = r and 6.
-// The readers precompute one offset per ds / db step for each lane, so the
-// unrolled loops read with immediate offsets only.
+// sigma below makes both conflict-free under that model for every ds, db
+// and R0 (checked on the host, with the copy placement and the readers'
+// offsets below, by tests/c_abi/swizzle_check.cpp): for D = 128, sigma(r) =
+// (r mod 16) xor (12 (r mod 2)); for D = 64 (two rows per bank sweep),
+// sigma(r) = r and 6.  The readers precompute one offset per ds / db step
+// for each lane, so the unrolled loops read with immediate offsets only.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ int swz_sigma(int r) {
+__host__ __device__ __forceinline__ int swz_sigma(int r) {
   static_assert(D == 64 || D == 128, "bf16 tiles are 64 or 128 wide");
   if constexpr (D == 128) return (r & 15) ^ (12 * (r & 1));
   else return r & 6;
+}
+
+// Element offset, in a swizzled tile, of the chunk that holds columns
+// 8 c .. 8 c + 7 of row r.
+template <int D>
+__host__ __device__ __forceinline__ int swz_chunk(int r, int c) {
+  return r * D + 8 * (c ^ swz_sigma<D>(r));
 }
 
 // Natural read of the operand "row R0 + l16, 8 elements at column 32 ds + 8 g"
@@ -138,10 +146,12 @@ __device__ __forceinline__ int swz_sigma(int r) {
 template <int D>
 struct NatReader {
   static constexpr int NDS = D / 32;
+  // element offset that lane (g, l16) reads at step ds, for R0 = 0
+  __host__ __device__ static int offset(int l16, int g, int ds) { return swz_chunk<D>(l16, 4 * ds + g); }
   int off[NDS];   // element offsets for R0 = 0
   __device__ __forceinline__ NatReader(int l16, int g) {
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) off[ds] = l16 * D + 8 * ((4 * ds + g) ^ swz_sigma<D>(l16));
+    for (int ds = 0; ds < NDS; ++ds) off[ds] = offset(l16, g, ds);
   }
   // r0 and ds must be compile-time constants after unrolling.
   __device__ __forceinline__ bf16x8 read(const __bf16* tile, int r0, int ds) const {
@@ -151,15 +161,21 @@ struct NatReader {
 
 // Transposed read: lane (g, l16) receives the 4 elements of column
 // 16 db + l16 in rows R0 + 4 g .. R0 + 4 g + 3 (R0 a multiple of 16).
+// (The lanes of a 16-lane group give ds_read_b64_tr_b16 the rows of a 4 x 16
+// block in order: lane j points at row j / 4, columns 4 (j mod 4) .. +3, and
+// receives column j.)
 template <int D>
 struct TrReader {
   static constexpr int NDB = D / 16;
+  // element offset that lane (g, l16) points at for column block db, R0 = 0
+  __host__ __device__ static int offset(int l16, int g, int db) {
+    const int row = 4 * g + (l16 >> 2);
+    return swz_chunk<D>(row, 2 * db + ((l16 >> 1) & 1)) + 4 * (l16 & 1);
+  }
   int off[NDB];
   __device__ __forceinline__ TrReader(int l16, int g) {
-    const int row = 4 * g + (l16 >> 2);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      off[db] = row * D + 8 * ((2 * db + ((l16 >> 1) & 1)) ^ swz_sigma<D>(row)) + 4 * (l16 & 1);
+    for (int db = 0; db < NDB; ++db) off[db] = offset(l16, g, db);
   }
   __device__ __forceinline__ bf16x4 read(const __bf16* tile, int r0, int db) const {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -215,14 +231,18 @@ struct AsyncTileCopy {
   int src_off[PER_WAVE];   // element offset of this lane's chunk in the global tile
   int lds_off[PER_WAVE];   // element offset of this wave's 64-chunk slot block (uniform)
 
+  // element offset, in the global tile, of the chunk that LDS chunk slot p
+  // receives (slot p sits at LDS element offset 8 p)
+  __host__ __device__ static int source_offset(int p) {
+    const int r = p / NCH;
+    const int c = (p % NCH) ^ swz_sigma<D>(r);
+    return r * D + c * 8;
+  }
   __device__ __forceinline__ AsyncTileCopy(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int slot0 = (i * NW + wave) * 64;
-      const int p = slot0 + lane;
-      const int r = p / NCH;
-      const int c = (p % NCH) ^ swz_sigma<D>(r);
-      src_off[i] = r * D + c * 8;
+      src_off[i] = source_offset(slot0 + lane);
       // uniform per wave: read into a scalar register once, so that no copy
       // needs a lane read to form its M0 value
       lds_off[i] = __builtin_amdgcn_readfirstlane(slot0 * 8);
