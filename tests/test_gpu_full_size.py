@@ -1,13 +1,15 @@
 """Full-size parity: every head of the headline configuration (BH 32,
-N 8192, d 128, bf16, causal and non-causal) and every head of the long
-context configuration (BH 8, N 32768, d 128, bf16, causal), with every output
-element compared against the fp64 oracle at the default tilings that
-bench.py times.  The oracle runs head by head on the host
+N 8192, d 128, bf16, causal and non-causal), every head of the long
+context configuration (BH 8, N 32768, d 128, bf16, causal) and two long
+heads at d = 64 (N 16384, both modes: 256 key tiles per query row for the
+d = 64 kernels), with every output element compared against the fp64
+oracle at the default tilings that bench.py times.  The oracle runs head by head on the host
 (tests/oracle_heads.py); the GPU results are computed once per test and
 copied to the host before the oracle starts."""
 
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 import pytest
@@ -68,3 +70,9 @@ def test_headline_every_head(causal):
 def test_long_context_every_head():
     w = WORKLOADS["long_32768_d128"]
     _check_heads(w, True, list(range(w.bh)))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_d64_every_head(causal):
+    w = SimpleNamespace(name="long_16384_d64", bh=2, n=16384, d=64, dtype="bf16")
+    _check_heads(w, causal, list(range(w.bh)))
