@@ -2,8 +2,9 @@
 N 8192, d 128, bf16, causal and non-causal), every head of the long
 context configuration (BH 8, N 32768, d 128, bf16, causal) and two long
 heads at d = 64 (N 16384, both modes: 256 key tiles per query row for the
-d = 64 kernels), with every output element compared against the fp64
-oracle at the default tilings that bench.py times.  The oracle runs head by head on the host
+d = 64 kernels), and two float32 heads at N 4096 (d 64 and 128, both
+modes), with every output element compared against the fp64 oracle at the
+default tilings (for bf16, the ones that bench.py times).  The oracle runs head by head on the host
 (tests/oracle_heads.py); the GPU results are computed once per test and
 copied to the host before the oracle starts."""
 
@@ -22,6 +23,7 @@ from workloads import WORKLOADS, cast_io, make_inputs, to_f64
 pytestmark = pytest.mark.gpu
 
 TOL = dict(o=1e-2, lse=1e-3, grad=3e-2)
+TOL_F32 = dict(o=1e-5, lse=1e-5, grad=1e-4)
 
 
 def _say(msg):
@@ -40,7 +42,7 @@ def _gpu_outputs(w, causal):
     return out
 
 
-def _check_heads(w, causal, heads):
+def _check_heads(w, causal, heads, tol=TOL):
     _say(f"[{w.name} causal={causal}] GPU forward + backward")
     q, k, v, do, o, lse, dq, dk, dv = _gpu_outputs(w, causal)
     for t in (o, lse, dq, dk, dv):
@@ -56,9 +58,9 @@ def _check_heads(w, causal, heads):
             worst[name] = max(worst[name], err[name])
         _say(f"[{w.name} causal={causal}] head {h} ({time.time() - t0:.0f} s): " +
              " ".join(f"{a}={b:.2e}" for a, b in err.items()))
-    assert worst["o"] <= TOL["o"] and worst["lse"] <= TOL["lse"], worst
+    assert worst["o"] <= tol["o"] and worst["lse"] <= tol["lse"], worst
     for name in ("dq", "dk", "dv"):
-        assert worst[name] <= TOL["grad"], (name, worst)
+        assert worst[name] <= tol["grad"], (name, worst)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -76,3 +78,10 @@ def test_long_context_every_head():
 def test_long_d64_every_head(causal):
     w = SimpleNamespace(name="long_16384_d64", bh=2, n=16384, d=64, dtype="bf16")
     _check_heads(w, causal, list(range(w.bh)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp32_long_every_head(causal, d):
+    w = SimpleNamespace(name=f"fp32_4096_d{d}", bh=2, n=4096, d=d, dtype="fp32")
+    _check_heads(w, causal, list(range(w.bh)), tol=TOL_F32)
